@@ -1,0 +1,50 @@
+"""NumPy float64 oracle for the fused attention forward.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke entry point
+and the benchmark's CPU-baseline leg, never by the HIP library or its binding.
+It is written independently of ``fa_oracle.c`` (the C oracle) so the two can
+cross-check each other; they share no code.
+
+Definition followed (plain, materialised, float64):
+  * "[CS336] Assignment 2: Systems", section "FlashAttention V2 / High level":
+    S = Q K^T scaled, P = row-softmax(S), O = P V, and the per-row logsumexp
+    L_i = log sum_j exp(S_ij).
+  * "Understanding Triton Tutorials Part 2", section "Fused Attention 2": the
+    causal mask is the lower triangle (key j visible to query i iff j <= i)
+    and the softmax is taken after subtracting the row maximum.
+Readings where the pages are silent: top-left causal alignment when
+seq_q != seq_k; keys j >= seq_k do not exist; natural-log lse; the scale
+multiplies the exact dot product; P is not rounded before P V.
+"""
+import numpy as np
+
+
+def attention_forward(q, k, v, sm_scale, causal, row_block=256):
+    """q: [B, H, Sq, D], k/v: [B, H, Sk, D] float64 arrays.
+
+    Returns (o [B, H, Sq, D], lse [B, H, Sq]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if Sk < 1:
+        raise ValueError("softmax over an empty key set is undefined")
+    o = np.empty((B, H, Sq, D), dtype=np.float64)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    key_idx = np.arange(Sk)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Sq, row_block):
+                rows = np.arange(r0, min(Sq, r0 + row_block))
+                scores = (q[b, h, rows] @ k[b, h].T) * sm_scale
+                if causal:
+                    hidden = key_idx[None, :] > rows[:, None]
+                    scores = np.where(hidden, -np.inf, scores)
+                row_max = scores.max(axis=1, keepdims=True)
+                unnorm = np.exp(scores - row_max)
+                denom = unnorm.sum(axis=1, keepdims=True)
+                o[b, h, rows] = (unnorm / denom) @ v[b, h]
+                lse[b, h, rows] = row_max[:, 0] + np.log(denom[:, 0])
+    return o, lse
