@@ -1,0 +1,113 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused attention forward library
+ *         (libfa_mi355x.so).
+ *
+ * The operation is the FlashAttention-2 style forward pass:
+ *     O = softmax(sm_scale * Q K^T [+ causal mask]) V,   lse_i = log sum_j exp(s_ij)
+ * as defined in "[CS336] Assignment 2: Systems", section "FlashAttention V2"
+ * (subsections "High level" and "Forward Pass": tiles of Q stay resident
+ * while K/V tiles stream past, a running row max and row sum implement the
+ * softmax online, and the logsumexp L is the second output), and in
+ * "Understanding Triton Tutorials Part 2", section "Fused Attention 2"
+ * (exp2 with log2(e) folded into the scale, normalisation deferred to the
+ * end, causal blocks above the diagonal skipped).  The score matrix is never
+ * written to memory.
+ *
+ * All entry points are plain C; no framework types appear in any signature.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type shared by q, k, v and o. */
+typedef enum {
+  FA_DTYPE_F32 = 0,  /* IEEE binary32; scores and P stay fp32 (fp32 MFMA) */
+  FA_DTYPE_F16 = 1,  /* IEEE binary16; P rounded to fp16 for the P.V product */
+  FA_DTYPE_BF16 = 2  /* bfloat16;      P rounded to bf16 for the P.V product */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* q, k, v or o is NULL */
+  FA_ERR_SHAPE = 2,     /* a size is negative, seq_k < 1, or a size exceeds 2^31-1 */
+  FA_ERR_DTYPE = 3,     /* dtype not one of fa_dtype_t */
+  FA_ERR_HEAD_DIM = 4,  /* head_dim outside 1..256, or not a multiple of 8 (16-bit) / 4 (fp32) */
+  FA_ERR_LAYOUT = 5,    /* dim stride != 1, negative stride, or misaligned pointer/stride */
+  FA_ERR_HIP = 6,       /* the HIP runtime reported an error when launching */
+  FA_ERR_SCALE = 7      /* sm_scale is NaN or infinite */
+} fa_status_t;
+
+/* Strides of one 4-D tensor, in ELEMENTS (not bytes), for the logical
+ * dimensions (batch, head, seq, dim).  Each tensor carries its own strides:
+ * sharing one head offset across Q, K, V and O breaks whenever their head
+ * strides differ (the failure reported in "BUG in flash attention kernel",
+ * triton-lang/triton issue 2626, for the (heads, seq, d) layout). */
+typedef struct {
+  int64_t batch, head, seq, dim;
+} fa_strides_t;
+
+/*
+ * fa_fwd -- enqueue the attention forward on `stream` and return.
+ *
+ *   q    [batch, heads, seq_q, head_dim]  device pointer, dtype, via q_st
+ *   k    [batch, heads, seq_k, head_dim]  device pointer, dtype, via k_st
+ *   v    [batch, heads, seq_k, head_dim]  device pointer, dtype, via v_st
+ *   o    [batch, heads, seq_q, head_dim]  device pointer, dtype, via o_st (output)
+ *   lse  [batch, heads, seq_q] fp32, contiguous, natural log (output);
+ *        may be NULL, in which case it is not written.
+ *
+ * Semantics per query row i of each (batch, head):
+ *   visible keys A(i) = { j < seq_k : causal == 0 or j <= i }   (top-left
+ *   alignment when seq_q != seq_k, so key 0 is always visible);
+ *   s_ij = sm_scale * sum_t q[i,t] k[j,t];  o[i,:] = sum_{j in A(i)} p_ij v[j,:]
+ *   with p_ij = exp(s_ij - max) / sum exp(s_ij - max);  lse[i] = log sum exp(s_ij).
+ * Accumulation is fp32.  For 16-bit inputs P is rounded to the input type
+ * before the P.V product; O is rounded to nearest-even into the input type.
+ *
+ * Ownership: every pointer is caller-owned device memory.  The library does
+ * not allocate, free or synchronise; it only launches kernels on `stream`
+ * (a hipStream_t; NULL means the default stream).  A fault in the kernel
+ * surfaces at the caller's next synchronisation.  o must not overlap q, k, v
+ * or lse (undefined, not checked).
+ *
+ * Validation happens on the host before any HIP call, in this order:
+ *   batch, heads, seq_q < 0, seq_k < 1, or any size, the grid or an index
+ *   that would exceed int32                      -> FA_ERR_SHAPE
+ *   dtype unknown                                -> FA_ERR_DTYPE
+ *   head_dim < 1, > 256, or not a multiple of 8 (f16/bf16) or 4 (f32)
+ *                                                -> FA_ERR_HEAD_DIM
+ *   a dim stride != 1, any negative stride, a batch/head/seq stride not a
+ *   multiple of 8 elements (f16/bf16)            -> FA_ERR_LAYOUT
+ *   sm_scale NaN or infinite                     -> FA_ERR_SCALE
+ *   batch, heads or seq_q == 0                   -> FA_OK, nothing launched
+ *                                                   (pointers may be NULL)
+ *   q/k/v/o NULL                                 -> FA_ERR_NULL
+ *   a base pointer not 16-byte aligned (f16/bf16) or 4-byte aligned (f32),
+ *   lse not 4-byte aligned                       -> FA_ERR_LAYOUT
+ * A failed launch returns FA_ERR_HIP.  On any non-OK return nothing has been
+ * enqueued and fa_last_error() describes the problem.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                   fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
+                   float sm_scale, int causal, fa_dtype_t dtype, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(fa_status_t status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none).  The
+ * pointer stays valid until the next fa_* call on the same thread. */
+const char* fa_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_MI355X_H */

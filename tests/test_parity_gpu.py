@@ -1,0 +1,163 @@
+"""Parity of the HIP attention forward with the CPU oracle (MI355X only).
+
+Every case calls the library through its C ABI binding and compares O and
+the logsumexp with the oracle at the stated tolerances: max-abs 1e-4 for
+fp32; max-abs 2e-2 and mean-abs 2e-3 for fp16/bf16.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from tiled_attention_04_amd import synth
+from gpu_cases import full_parity, sampled_parity, sampled_rows, say, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_attention_04_amd as fa
+    fa.lib()  # fail loudly if the HIP library is missing
+
+
+# ---- the five workloads ------------------------------------------------------
+
+@pytest.mark.parametrize("key", ["c1", "c2", "c3"])
+def test_workload_full(key):
+    full_parity(synth.make_inputs(key), name=key)
+
+
+def test_workload_c4_sampled():
+    inp = synth.make_inputs("c4")
+    rows = sampled_rows(inp.workload, np.random.default_rng(4), 1500)
+    sampled_parity(inp, rows, name="c4")
+
+
+def test_workload_c5_sampled():
+    inp = synth.make_inputs("c5")
+    w = inp.workload
+    # rows that see a stressed (x8) key on or after it, for head (0, 0) and (0, 15)
+    extra = []
+    for (b, h) in [(0, 0), (0, 15)]:
+        idx = inp.stressed_rows[(b, h)]
+        base = (b * w.heads + h) * w.seq_q
+        extra += [base + int(j) for j in idx[:40]] + [base + int(j) + 1 for j in idx[:20]]
+    rows = sampled_rows(w, np.random.default_rng(5), 400, extra=extra)
+    sampled_parity(inp, rows, name="c5")
+
+
+# ---- edges -------------------------------------------------------------------
+
+EDGE_SEQ = [(1, 1), (1, 64), (10, 63), (100, 65), (129, 127), (64, 129), (77, 300), (300, 77)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sq,sk", EDGE_SEQ)
+def test_ragged_sequences(dtype, causal, sq, sk):
+    w = synth.custom("ragged", dtype, "bhsd", 2, 3, sq, sk, 64, causal=causal,
+                     seed=100 + sq * 7 + sk)
+    full_parity(synth.make_inputs(w), name=f"ragged {dtype} sq={sq} sk={sk} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [8, 16, 24, 32, 40, 64, 72, 80, 96, 112, 128, 136, 160, 192, 256])
+def test_head_dims_bf16(d):
+    w = synth.custom("hd", "bf16", "bhsd", 1, 2, 150, 190, d, causal=(d % 16 == 0), seed=200 + d)
+    full_parity(synth.make_inputs(w), name=f"head_dim bf16 d={d}")
+
+
+@pytest.mark.parametrize("d", [8, 64, 80, 128])
+def test_head_dims_fp16(d):
+    w = synth.custom("hd", "fp16", "bhsd", 1, 2, 150, 190, d, causal=True, seed=300 + d)
+    full_parity(synth.make_inputs(w), name=f"head_dim fp16 d={d}")
+
+
+@pytest.mark.parametrize("d", [4, 12, 32, 60, 64, 100, 128, 256])
+def test_head_dims_fp32(d):
+    w = synth.custom("hd", "fp32", "bhsd", 1, 2, 150, 190, d, causal=(d % 8 == 0), seed=400 + d)
+    full_parity(synth.make_inputs(w), name=f"head_dim fp32 d={d}")
+
+
+def test_seq_heads_dim_layout_cross_attention():
+    """[seq, heads, d] with seq_q != seq_k (the layout family of the issue)."""
+    w = synth.custom("shd", "fp16", "shd", 1, 8, 100, 700, 32, std=0.5, sm_scale=0.5, seed=500)
+    full_parity(synth.make_inputs(w), name="shd fp16 q_ctx=100")
+
+
+def test_heads_seq_dim_layout_distinct_head_strides():
+    """(heads, seq, d) with q_ctx != seqlen: Q/O and K/V head strides differ, the
+    case the "BUG in flash attention kernel" issue got wrong."""
+    import torch
+    w = synth.custom("hsd", "fp16", "bhsd", 1, 8, 4095, 4096, 32, std=0.5, sm_scale=0.5, seed=501)
+    full_parity(synth.make_inputs(w), name="hsd fp16 q_ctx=4095 vs 4096")
+    w2 = synth.custom("hsd", "fp16", "bhsd", 1, 16, 10, 4096, 32, std=0.5, sm_scale=0.5, seed=502)
+    full_parity(synth.make_inputs(w2), name="hsd fp16 q_ctx=10")
+
+
+def test_strided_views():
+    """Inputs that are views with padded rows and a permuted layout."""
+    import torch
+
+    def views(q, k, v):
+        # embed each tensor in a wider buffer (row stride 72 instead of 64)
+        def widen(t):
+            buf = torch.zeros(t.shape[:-1] + (t.shape[-1] + 8,), dtype=t.dtype, device=t.device)
+            buf[..., : t.shape[-1]] = t
+            return buf[..., : t.shape[-1]]
+        return widen(q), widen(k), widen(v)
+
+    w = synth.custom("views", "bf16", "bhsd", 2, 2, 130, 200, 64, causal=True, seed=503)
+    full_parity(synth.make_inputs(w), views=views, name="strided views bf16")
+
+
+def test_lse_null_path():
+    w = synth.custom("nolse", "bf16", "bhsd", 1, 2, 70, 90, 64, seed=504)
+    full_parity(synth.make_inputs(w), with_lse=False, name="lse=NULL")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.0])
+def test_scale_values(scale):
+    w = synth.custom("scale", "bf16", "bhsd", 1, 2, 100, 150, 64, causal=True, seed=505)
+    full_parity(synth.make_inputs(w), sm_scale=scale, name=f"sm_scale={scale}")
+
+
+def test_large_logit_stress_small():
+    w = synth.custom("stress", "bf16", "bhsd", 1, 4, 512, 512, 128, causal=True, seed=506,
+                     stress_frac=0.02, stress_factor=8.0)
+    full_parity(synth.make_inputs(w), name="stress x8 small")
+    w2 = synth.custom("stress", "fp16", "bhsd", 1, 4, 300, 300, 64, std=1.0, sm_scale=0.25,
+                      causal=False, seed=507, stress_frac=0.05, stress_factor=32.0)
+    full_parity(synth.make_inputs(w2), name="stress x32 fp16")
+
+
+def test_many_heads_xcd_mapping():
+    """n_bh % 8 == 0 takes the XCD-grouped workgroup mapping; 7 heads does not."""
+    for heads in (8, 7):
+        w = synth.custom("xcd", "bf16", "bhsd", 2, heads, 300, 300, 64, causal=True,
+                         seed=508 + heads)
+        full_parity(synth.make_inputs(w), name=f"heads={heads} batch=2")
+
+
+def test_empty_problems_are_noops():
+    import torch
+    import tiled_attention_04_amd as fa
+    for shape_q in [(0, 2, 8, 64), (1, 0, 8, 64), (1, 2, 0, 64)]:
+        q = torch.zeros(shape_q, dtype=torch.bfloat16, device="cuda")
+        kv = torch.zeros((shape_q[0], shape_q[1], 8, 64), dtype=torch.bfloat16, device="cuda")
+        o = torch.full_like(q, 3.0)
+        fa.forward(q, kv, kv, out=o)
+        torch.cuda.synchronize()
+        assert bool((o == 3.0).all())
+
+
+def test_repeat_is_bitwise_deterministic():
+    import torch
+    w = synth.custom("det", "bf16", "bhsd", 1, 8, 1000, 1000, 128, causal=True, seed=509)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_gpu(inp)
+    o2, l2 = run_gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -1,0 +1,132 @@
+"""MI355X (gfx950) fused attention forward: thin ctypes binding of libfa_mi355x.so.
+
+The binding only marshals arguments: every step of the attention forward runs
+in the library's HIP kernels.  PyTorch supplies device memory and the stream.
+There is no CPU fallback -- calling into the binding without the built
+library raises.
+
+``fa_fwd`` mirrors the C entry point of the same name (raw pointers, sizes and
+per-tensor element strides); ``forward`` is the tensor-level convenience
+wrapper.
+"""
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
+
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
+          4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_LAYOUT", 6: "FA_ERR_HIP", 7: "FA_ERR_SCALE"}
+EXPORTS = ("fa_fwd", "fa_status_string", "fa_last_error", "fa_version")
+
+
+class FaStrides(ctypes.Structure):
+    """Element strides of one tensor for (batch, head, seq, dim)."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64),
+                ("seq", ctypes.c_int64), ("dim", ctypes.c_int64)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libfa_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m tiled_attention_04_amd.build` "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fa_fwd.restype = ctypes.c_int
+        L.fa_fwd.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [FaStrides] * 4 +
+                             [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_status_string.argtypes = [ctypes.c_int]
+        L.fa_last_error.restype = ctypes.c_char_p
+        L.fa_last_error.argtypes = []
+        L.fa_version.restype = ctypes.c_int
+        L.fa_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def fa_fwd(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_st, o_st,
+           sm_scale, causal, dtype, stream):
+    """Direct call of the C entry point; returns the integer status."""
+    st = [s if isinstance(s, FaStrides) else FaStrides(*s) for s in (q_st, k_st, v_st, o_st)]
+    return lib().fa_fwd(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, *st,
+                        float(sm_scale), int(causal), int(dtype), stream)
+
+
+def last_error():
+    return lib().fa_last_error().decode()
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
+             torch.bfloat16: FA_DTYPE_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _dims(t, layout):
+    """(batch, heads, seq, dim) sizes and element strides of t under `layout`."""
+    if layout == "bhsd":
+        B, H, S, D = t.shape
+        sb, sh, ss, sd = t.stride()
+    elif layout == "bshd":
+        B, S, H, D = t.shape
+        sb, ss, sh, sd = t.stride()
+    elif layout == "shd":
+        S, H, D = t.shape
+        ss, sh, sd = t.stride()
+        B, sb = 1, 0
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    return (B, H, S, D), FaStrides(sb, sh, ss, sd)
+
+
+def forward(q, k, v, causal=False, sm_scale=None, layout="bhsd", out=None, lse=None,
+            return_lse=True):
+    """Attention forward on the current HIP stream.
+
+    q: [B, H, Sq, D] ("bhsd"), [B, Sq, H, D] ("bshd") or [Sq, H, D] ("shd");
+    k, v: the same with Sk.  sm_scale defaults to 1/sqrt(D).
+    Returns (o, lse) with o like q and lse fp32 [B, H, Sq]; or o alone when
+    return_lse is False (then lse is not computed unless passed in).
+    """
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be device tensors")
+    (B, H, Sq, D), q_st = _dims(q, layout)
+    (Bk, Hk, Sk, Dk), k_st = _dims(k, layout)
+    (Bv, Hv, Sv, Dv), v_st = _dims(v, layout)
+    if (Bk, Hk, Dk) != (B, H, D) or (Bv, Hv, Sv, Dv) != (B, H, Sk, D):
+        raise ValueError("q, k, v shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    (_, _, _, _), o_st = _dims(out, layout)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                lse.data_ptr() if lse is not None else None, B, H, Sq, Sk, D,
+                q_st, k_st, v_st, o_st, sm_scale, causal, _dtype_code(q), stream)
+    if rc != 0:
+        raise FaError(rc, last_error())
+    return (out, lse) if return_lse else out

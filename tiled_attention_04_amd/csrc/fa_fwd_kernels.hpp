@@ -1,0 +1,531 @@
+// fa_fwd_kernels.hpp -- gfx950 (MI355X) kernels of the fused attention forward.
+//
+// Method: the FlashAttention-2 forward of "[CS336] Assignment 2: Systems",
+// section "FlashAttention V2 / Forward Pass", and of "Understanding Triton
+// Tutorials Part 2", section "Fused Attention 2": a tile of queries stays
+// resident, K/V tiles stream past it, a running row max m and row sum l keep
+// the softmax online (with exp2 and log2(e) folded into the scale), the
+// un-normalised output accumulates in fp32 and is divided by l once at the
+// end, and the per-row logsumexp is emitted.  Causal tiles above the
+// diagonal are never visited.
+//
+// MI355X design (not taken from the pages):
+//  * one workgroup of NW waves per (batch*head, query tile of 32*NW rows);
+//    each wave owns 32 query rows for the whole key loop;
+//  * scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_{bf16,f16}: K (from LDS) is the A operand and the
+//    wave's Q fragment (registers, loaded once) is the B operand.  In the
+//    32x32 result layout lane l holds 16 keys of query (l % 32), so row max
+//    and row sum are in-lane except for one exchange with lane l ^ 32;
+//  * P stays in registers: the result layout of S^T, rounded to bf16/f16, is
+//    directly the B operand of O^T += V^T P^T (keys permuted consistently on
+//    both operands); V^T fragments come from LDS with ds_read_b64_tr_b16,
+//    which transposes 4 keys x 16 dims per 16-lane group on the fly;
+//  * K/V tiles are double-buffered in LDS through registers (128-bit global
+//    loads issued one tile ahead), rows padded so the MFMA operand reads of
+//    one wave spread over the banks;
+//  * keys >= seq_k and (causal) keys > query are masked to -inf; key rows
+//    beyond seq_k and dims beyond head_dim are zero-filled;
+//  * the running max is refreshed lazily: O and l are rescaled only when the
+//    row max grows by more than RESCALE_LOG2 (base 2), so P <= 2^RESCALE_LOG2.
+//    Any reference value at or below the true running max gives the same
+//    O = acc / l and lse = m + log l in exact arithmetic; the pages rescale on
+//    every tile;
+//  * workgroup ids are remapped so all query tiles of one (batch, head) run
+//    on the same XCD (shared L2 for its K/V stream), heaviest causal tiles
+//    first.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (P <= 256)
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_ss;  // element strides: batch, head, seq (dim stride is 1)
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int32_t heads, seq_q, seq_k, head_dim;
+  int32_t n_qtiles;  // ceil(seq_q / BM)
+  int32_t n_bh;      // batch * heads
+  float c;           // |sm_scale| * log2(e), at least 1e-30
+  int32_t neg_scale;  // sm_scale < 0: Q is negated in registers
+  int32_t causal;
+  int32_t xcd_remap;  // n_bh % 8 == 0: keep one (batch, head) on one XCD
+};
+
+// Map the linear workgroup id to (batch*head, query tile).  Workgroups are
+// handed to the 8 XCDs round-robin, so ids with the same residue mod 8 share
+// an XCD and its L2; all tiles of one (batch, head) get the same residue.
+// Causal: heaviest (last) query tiles are dispatched first.
+__device__ inline void map_workgroup(const FwdArgs& a, int wg, int& bh, int& qt) {
+  int rank;
+  if (a.xcd_remap) {
+    const int per = a.n_bh >> 3;
+    const int xcd = wg & 7, slot = wg >> 3;
+    bh = xcd * per + slot % per;
+    rank = slot / per;
+  } else {
+    bh = wg % a.n_bh;
+    rank = wg / a.n_bh;
+  }
+  qt = a.causal ? a.n_qtiles - 1 - rank : rank;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  typedef bf16x8_t frag;
+  __device__ static inline f32x16_t mma(const frag& a, const frag& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // round-to-nearest-even pair conversion (v_cvt_pk_bf16_f32)
+  __device__ static inline uint32_t pack2(float x, float y) {
+    f32x2_t v = {x, y};
+    bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+template <>
+struct Mfma<_Float16> {
+  typedef f16x8_t frag;
+  __device__ static inline f32x16_t mma(const frag& a, const frag& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack2(float x, float y) {
+    f32x2_t v = {x, y};
+    f16x2_t r = __builtin_convertvector(v, f16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+// Smallest stride >= min_bytes that is congruent to `residue` modulo 256.
+constexpr int pad_to_residue(int min_bytes, int residue) {
+  return ((min_bytes - residue + 255) / 256) * 256 + residue;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit inputs (bf16 / f16).  D = head_dim rounded up to 16, NW waves.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW>
+struct Tile16 {
+  static constexpr int BM = 32 * NW;           // query rows per workgroup
+  static constexpr int BN = 64;                // keys per K/V tile
+  static constexpr int NT = 64 * NW;           // threads per workgroup
+  static constexpr int KSTEPS = D / 16;        // k-steps of the S^T MFMA (16 dims each)
+  static constexpr int DBLK = (D + 31) / 32;   // 32-dim blocks of the O^T accumulator
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  // K rows: stride = 16 (mod 256) bytes, so the 32 lanes reading one 16-byte
+  // chunk of 32 consecutive rows fall on distinct bank groups.
+  static constexpr int KROW = D * 2 + 16;
+  // V rows: stride = 64 (mod 256) bytes, so the 4 rows x 32 bytes gathered by
+  // each 16-lane group of a transposing read fall on distinct banks.
+  static constexpr int VROW = pad_to_residue(DBLK * 64, 64);
+  static constexpr int KBYTES = BN * KROW;
+  static constexpr int VBYTES = BN * VROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int LOADS = (BN * CH + NT - 1) / NT;  // 16-byte chunks per thread per tensor
+  static_assert(D % 16 == 0 && D <= 256, "head_dim padding");
+  static_assert(KROW % 16 == 0 && VROW % 16 == 0, "16-byte aligned rows");
+};
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
+  using G = Tile16<T, D, NW>;
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
+  constexpr int BN = G::BN, NT = G::NT, CH = G::CH, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
+  constexpr int KROW = G::KROW, VROW = G::VROW;
+
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  FA_LDS char* lds = (FA_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;   // query column owned by this lane
+  const int hi = lane >> 5;    // which half of the 32x32 result rows
+
+  int bh, qt;
+  map_workgroup(a, blockIdx.x, bh, qt);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+
+  const T* qg = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const T* kg = (const T*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const T* vg = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  T* og = (T*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+
+  const int q0 = qt * G::BM;
+  const int qw = q0 + wave * 32;        // first query row of this wave
+  const int my_q = qw + l32;            // query row of this lane
+  const int wave_last = min(qw + 31, a.seq_q - 1);
+  const bool wave_live = qw < a.seq_q;
+
+  // keys this workgroup must visit (causal: up to its last real query)
+  const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + G::BM)) : a.seq_k;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  // ---- resident Q fragment: B operand of S^T, lane = (query l32, dims 8*hi..+7 of each step)
+  frag qf[KSTEPS];
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st) {
+    const int col = st * 16 + hi * 8;
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (my_q < a.seq_q && col < a.head_dim)
+      raw = *(const u32x4_t*)(qg + (int64_t)my_q * a.q_ss + col);
+    if (a.neg_scale) raw ^= (u32x4_t){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    qf[st] = __builtin_bit_cast(frag, raw);
+  }
+
+  // ---- zero the LDS once (pads and V columns beyond D are read but never written)
+  for (int off = tid * 16; off < G::LDS_BYTES; off += NT * 16)
+    *(FA_LDS u32x4_t*)(lds + off) = (u32x4_t){0u, 0u, 0u, 0u};
+
+  // ---- K/V tile staging through registers
+  u32x4_t kreg[G::LOADS], vreg[G::LOADS];
+  auto load_tile = [&](int t) {
+    const int key0 = t * BN;
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) {
+      const int ci = tid + n * NT;
+      const int row = ci / CH, c = ci - (ci / CH) * CH;
+      const bool ok = (ci < BN * CH) && (key0 + row < a.seq_k) && (c * 8 < a.head_dim);
+      u32x4_t kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
+      if (ok) {
+        kz = *(const u32x4_t*)(kg + (int64_t)(key0 + row) * a.k_ss + c * 8);
+        vz = *(const u32x4_t*)(vg + (int64_t)(key0 + row) * a.v_ss + c * 8);
+      }
+      kreg[n] = kz;
+      vreg[n] = vz;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    FA_LDS char* kb = lds + stage * G::STAGE;
+    FA_LDS char* vb = kb + G::KBYTES;
+#pragma unroll
+    for (int n = 0; n < G::LOADS; ++n) {
+      const int ci = tid + n * NT;
+      if (ci < BN * CH) {
+        const int row = ci / CH, c = ci - (ci / CH) * CH;
+        *(FA_LDS u32x4_t*)(kb + row * KROW + c * 16) = kreg[n];
+        *(FA_LDS u32x4_t*)(vb + row * VROW + c * 16) = vreg[n];
+      }
+    }
+  };
+
+  // ---- online-softmax state (per lane: query l32; both halves agree on m)
+  f32x16_t acc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) acc[db] = (f32x16_t){};
+  float m_run = -INFINITY;  // reference max, base-2 scaled units
+  float l_run = 0.f;        // partial row sum over this lane's keys
+  const float c = a.c;
+
+  // lane-constant LDS offsets
+  const int k_lane = l32 * KROW + hi * 16;
+  const int s16 = lane & 15;
+  const int v_lane = (4 * hi + (s16 >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+
+  if (n_tiles > 0) load_tile(0);
+  __syncthreads();  // zero-fill complete before the first tile lands
+  if (n_tiles > 0) store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const int key0 = t * BN;
+    const bool skip = !wave_live || (a.causal && key0 > wave_last);
+    if (!skip) {
+      FA_LDS char* kb = lds + (t & 1) * G::STAGE;
+      FA_LDS char* vb = kb + G::KBYTES;
+
+      // S^T = K Q^T for two 32-key blocks
+      f32x16_t s[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x16_t sc = (f32x16_t){};
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+          const frag kf = __builtin_bit_cast(
+              frag, *(FA_LDS u32x4_t*)(kb + k_lane + kb2 * 32 * KROW + st * 32));
+          sc = M::mma(kf, qf[st], sc);
+        }
+        s[kb2] = sc;
+      }
+
+      // masks: key tail and causal diagonal (only on tiles that need them)
+      const bool need_mask = (key0 + BN > a.seq_k) || (a.causal && key0 + BN - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool vis = key < a.seq_k && (!a.causal || key <= my_q);
+            s[kb2][r] = vis ? s[kb2][r] : -INFINITY;
+          }
+      }
+
+      // row max: in-lane over 32 keys, then with the partner half
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_tile = mx * c;  // c > 0, so max(s) * c = max(s * c)
+      const float m_new = fmaxf(m_run, m_tile);
+      const bool upd = m_new > m_run + kRescaleLog2;
+      if (__ballot(upd)) {
+        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
+        m_run = upd ? m_new : m_run;
+      }
+      const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+
+      // P = exp2(s*c - m), partial row sums, pack to the input type
+      uint32_t pk[2][8];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
+          lsum += p0 + p1;
+          pk[kb2][r >> 1] = M::pack2(p0, p1);
+        }
+      l_run += lsum;
+
+      // O^T += V^T P^T: four 16-key MFMA steps per 32-dim block
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4_t praw = {pk[u >> 1][4 * (u & 1) + 0], pk[u >> 1][4 * (u & 1) + 1],
+                              pk[u >> 1][4 * (u & 1) + 2], pk[u >> 1][4 * (u & 1) + 3]};
+        const frag pf = __builtin_bit_cast(frag, praw);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          FA_LDS char* p0 = vb + v_lane + (16 * u) * VROW + db * 64;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p0);
+          const i16x4_t up =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + 8 * VROW));
+          const u32x4_t vraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                                __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
+          acc[db] = M::mma(__builtin_bit_cast(frag, vraw), pf, acc[db]);
+        }
+      }
+    }
+    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
+  if (!wave_live) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (my_q < a.seq_q) {
+    const float inv = 1.0f / l_tot;
+    T* orow = og + (int64_t)my_q * a.o_ss;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hi;
+        if (d0 < a.head_dim) {
+          const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                             M::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+          *(u32x2_t*)(orow + d0) = w;
+        }
+      }
+    if (hi == 0 && a.lse != nullptr)
+      a.lse[(int64_t)bh * a.seq_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: same schedule with v_mfma_f32_32x32x2f32; scores, P and the
+// accumulator stay fp32 end to end.  D = head_dim rounded up to 32.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Tile32 {
+  static constexpr int NW = 4;
+  static constexpr int BM = 32 * NW;
+  static constexpr int BN = 64;
+  static constexpr int NT = 64 * NW;
+  static constexpr int KSTEPS = D / 2;
+  static constexpr int DBLK = D / 32;
+  static constexpr int KROW = D + 1;  // floats; odd stride spreads rows over banks
+  static constexpr int VROW = D;      // floats; lanes read consecutive columns
+  static constexpr int STAGE = BN * (KROW + VROW);  // floats
+  static constexpr int LDS_BYTES = STAGE * 4;  // single stage: fp32 is a small-problem path
+  static_assert(D % 32 == 0 && D <= 256, "head_dim padding");
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void fa_fwd_f32(FwdArgs a) {
+  using G = Tile32<D>;
+  constexpr int BN = G::BN, NT = G::NT, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
+  constexpr int KROW = G::KROW, VROW = G::VROW;
+
+  __shared__ __attribute__((aligned(16))) float smem[G::LDS_BYTES / 4];
+  FA_LDS float* lds = (FA_LDS float*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bh, qt;
+  map_workgroup(a, blockIdx.x, bh, qt);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const float* qg = (const float*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const float* kg = (const float*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const float* vg = (const float*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  float* og = (float*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+
+  const int q0 = qt * G::BM;
+  const int qw = q0 + wave * 32;
+  const int my_q = qw + l32;
+  const int wave_last = min(qw + 31, a.seq_q - 1);
+  const bool wave_live = qw < a.seq_q;
+  const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + G::BM)) : a.seq_k;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  float qf[KSTEPS];
+  const float qsign = a.neg_scale ? -1.f : 1.f;
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st) {
+    const int col = 2 * st + hi;
+    qf[st] = (my_q < a.seq_q && col < a.head_dim) ? qsign * qg[(int64_t)my_q * a.q_ss + col] : 0.f;
+  }
+
+  auto fill_tile = [&](int t, int stage) {
+    FA_LDS float* kb = lds + stage * G::STAGE;
+    FA_LDS float* vb = kb + BN * KROW;
+    const int key0 = t * BN;
+    for (int e = tid; e < BN * D; e += NT) {
+      const int row = e / D, col = e - (e / D) * D;
+      const bool ok = key0 + row < a.seq_k && col < a.head_dim;
+      kb[row * KROW + col] = ok ? kg[(int64_t)(key0 + row) * a.k_ss + col] : 0.f;
+      vb[row * VROW + col] = ok ? vg[(int64_t)(key0 + row) * a.v_ss + col] : 0.f;
+    }
+  };
+
+  f32x16_t acc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) acc[db] = (f32x16_t){};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.c;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();  // previous tile fully consumed
+    fill_tile(t, 0);
+    __syncthreads();
+    const int key0 = t * BN;
+    if (!wave_live || (a.causal && key0 > wave_last)) continue;
+    FA_LDS float* kb = lds;
+    FA_LDS float* vb = kb + BN * KROW;
+
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x16_t sc = (f32x16_t){};
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st)
+        sc = __builtin_amdgcn_mfma_f32_32x32x2f32(kb[(kb2 * 32 + l32) * KROW + 2 * st + hi],
+                                                  qf[st], sc, 0, 0, 0);
+      s[kb2] = sc;
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool vis = key < a.seq_k && (!a.causal || key <= my_q);
+        s[kb2][r] = vis ? s[kb2][r] : -INFINITY;
+      }
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c);
+    const bool upd = m_new > m_run + kRescaleLog2;
+    if (__ballot(upd)) {
+      const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
+      m_run = upd ? m_new : m_run;
+    }
+    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kb2][r] = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
+        lsum += s[kb2][r];
+      }
+    l_run += lsum;
+    // O^T += V^T P^T, one MFMA per result register r: k index = lane half
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vb[key * VROW + db * 32 + l32], s[kb2][r],
+                                                         acc[db], 0, 0, 0);
+      }
+  }
+
+  if (!wave_live) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (my_q < a.seq_q) {
+    const float inv = 1.0f / l_tot;
+    float* orow = og + (int64_t)my_q * a.o_ss;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = db * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (d < a.head_dim) orow[d] = acc[db][r] * inv;
+      }
+    if (hi == 0 && a.lse != nullptr)
+      a.lse[(int64_t)bh * a.seq_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+}  // namespace fa
