@@ -1,0 +1,240 @@
+"""Benchmark of the MI355X fused attention forward.
+
+Default workload: bf16 [batch 1, heads 16, seq 32768, head_dim 128], causal,
+sm_scale 1/sqrt(128), Q/K/V ~ N(0, 1) with 1% of the K rows of every head
+scaled by 8 (seeded synthetic inputs).  One step is one call of fa_fwd over
+that batch (the whole forward: O and the logsumexp).  Inputs are resident in
+HBM before the timed region starts.
+
+Prints one JSON line:
+  value      attention TFLOP/s = 4*b*h*s_q*s_k*d (halved for causal) / time
+  roofline   the kernel's achieved TFLOP/s against the MI355X dense bf16 MFMA
+             peak, with HBM traffic from rocprofv3 counters when they were
+             taken on the current kernel source
+  cpu_baseline  the CPU oracle (C, double, OpenMP) timed on a bounded sample
+             of the same workload on this host
+
+Other modes:
+  --workload c2|c3|c4   time another workload (not the default line)
+  --copy-calib          also run a plain device copy of 1 GiB (for counter
+                        calibration under rocprofv3 --pmc)
+  --summarize-pmc DIR   reduce rocprofv3 --pmc output under DIR to a summary
+"""
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (1 GPU)"
+KERNEL_SOURCES = ["tiled_attention_04_amd/csrc/fa_fwd_kernels.hpp",
+                  "tiled_attention_04_amd/csrc/fa_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c5.json")
+# context only: the pages' unfused attention timings on an RTX 3090 (fp32,
+# d_model 768, 12 heads, batch 4; sequence length not stated)
+CONTEXT_RTX3090 = {"qk_matmul_ms": 0.1428, "pv_matmul_ms": 0.0759, "softmax_ms": 0.0314,
+                   "source": "[CS336] Assignment 2: Systems, Nsight Systems Profile (unfused)"}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches
+    the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, target_s=15.0):
+    """Time the C oracle on a bounded sample of rows of the workload."""
+    import numpy as np
+    import oracle
+
+    w = inp.workload
+    heads = [(0, 0)]
+    q64 = inp.as_bhsd_f64("q", heads)
+    k64 = inp.as_bhsd_f64("k", heads)
+    v64 = inp.as_bhsd_f64("v", heads)
+    S = w.seq_q
+
+    def row_flops(rows):
+        keys = np.minimum(rows + 1, w.seq_k) if w.causal else np.full(rows.shape, w.seq_k)
+        return float(np.sum(4.0 * keys * w.head_dim))
+
+    def pick(n):  # evenly spaced rows: their mean causal length matches the workload's
+        return np.unique(np.linspace(0, S - 1, n).astype(np.int64))
+
+    pilot = pick(64)
+    t0 = time.perf_counter()
+    oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=pilot)
+    t_pilot = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(S, max(64, 64 * target_s / t_pilot)))
+    rows = pick(n)
+    t0 = time.perf_counter()
+    oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": row_flops(rows) / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{rows.size} evenly spaced query rows of head (0,0) of the same workload "
+                      f"(fp64 C oracle, materialised softmax), {dt:.1f} s wall"}
+
+
+def summarize_pmc(d):
+    """Reduce rocprofv3 --pmc counter CSVs under d: per-kernel mean of each counter."""
+    import csv
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                k = row.get("Kernel_Name", "?")
+                c = row.get("Counter_Name", "?")
+                v = float(row.get("Counter_Value", "nan"))
+                key = (k, c)
+                n, s = out.get(key, (0, 0.0))
+                out[key] = (n + 1, s + v)
+    res = {}
+    for (k, c), (n, s) in sorted(out.items()):
+        res.setdefault(k, {})[c] = {"mean": s / n, "samples": n}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--summarize-pmc", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (heads shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tiled_attention_04_amd as fa
+    from tiled_attention_04_amd import synth
+
+    fa.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    layout = "shd" if w.layout == "shd" else "bhsd"
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.forward(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout, out=o, lse=lse)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_region = region0.elapsed_time(region1)
+    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ms_avg = sum(per_launch) / len(per_launch)
+    ms_per_step = ms_region / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (ms_avg * 1e-3) / 1e12
+    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (events), wall {t_wall:.3f} s, "
+          f"kernel avg {ms_avg:.4f} ms, median {per_launch[len(per_launch)//2]:.4f}, "
+          f"min {per_launch[0]:.4f}", file=sys.stderr, flush=True)
+
+    if args.copy_calib:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 copies of {n} bytes", file=sys.stderr, flush=True)
+        del src, dst
+
+    traffic = load_traffic() if args.workload == "c5" else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_q": w.seq_q,
+                   "seq_k": w.seq_k, "head_dim": w.head_dim, "causal": w.causal,
+                   "sm_scale": w.sm_scale, "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms_avg": round(ms_avg, 5),
+                     "kernel_ms_min": round(per_launch[0], 5)},
+        "context": {"rtx3090_unfused_per_call": CONTEXT_RTX3090},
+    }
+    if not args.no_cpu_baseline and args.workload == "c5":
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
