@@ -81,8 +81,9 @@ typedef struct {
  *   dtype unknown                                -> FA_ERR_DTYPE
  *   head_dim < 1, > 256, or not a multiple of 8 (f16/bf16) or 4 (f32)
  *                                                -> FA_ERR_HEAD_DIM
- *   a dim stride != 1, any negative stride, a batch/head/seq stride not a
- *   multiple of 8 elements (f16/bf16)            -> FA_ERR_LAYOUT
+ *   a dim stride != 1, any negative stride, a seq stride >= 2^24 elements,
+ *   a batch/head/seq stride not a multiple of 8 elements (f16/bf16)
+ *                                                -> FA_ERR_LAYOUT
  *   sm_scale NaN or infinite                     -> FA_ERR_SCALE
  *   batch, heads or seq_q == 0                   -> FA_OK, nothing launched
  *                                                   (pointers may be NULL)

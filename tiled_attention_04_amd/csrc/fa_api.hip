@@ -29,8 +29,14 @@ constexpr int64_t kInt32Max = 2147483647;
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Tiles are addressed with 32-bit byte offsets from a per-tile base, so one
+// tile's rows must span less than 2 GiB: seq stride < 2^24 elements.
+constexpr int64_t kMaxSeqStride = (int64_t)1 << 24;
+
 fa_status_t check_strides(const char* name, const fa_strides_t& st, int64_t mult) {
   if (st.dim != 1) return fail(FA_ERR_LAYOUT, "%s: dim stride must be 1 (got %lld)", name, (long long)st.dim);
+  if (st.seq >= kMaxSeqStride)
+    return fail(FA_ERR_LAYOUT, "%s: seq stride %lld must be below 2^24 elements", name, (long long)st.seq);
   const int64_t s[3] = {st.batch, st.head, st.seq};
   const char* n[3] = {"batch", "head", "seq"};
   for (int i = 0; i < 3; ++i) {
@@ -53,15 +59,28 @@ fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& 
 }
 
 // Instantiated head-dim paddings: the smallest one >= head_dim is used.
+#ifndef FA_NW16
+#define FA_NW16 4  // waves per workgroup (32 query rows each)
+#endif
+#ifndef FA_OCC16
+#define FA_OCC16 2  // waves per SIMD the register budget is sized for
+#endif
+
+template <typename T, int D, int NW, int OCC>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void fa_fwd_16bit(fa::FwdArgs a) {
+  fa::fa_fwd_16bit_body<T, D, NW>(a);
+}
+
 template <typename T>
 fa_status_t launch_16bit(fa::FwdArgs& a, int64_t head_dim, void* stream) {
-  constexpr int NW = 4;
+  constexpr int NW = FA_NW16, OCC = FA_OCC16;
   a.n_qtiles = (int32_t)((a.seq_q + 32 * NW - 1) / (32 * NW));
   const int64_t grid = (int64_t)a.n_bh * a.n_qtiles;
   if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
   a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
 #define FA_CASE(DP)                                                            \
-  if (head_dim <= DP) return launch(fa::fa_fwd_16bit<T, DP, NW>, grid, 64 * NW, a, stream);
+  if (head_dim <= DP) return launch(fa_fwd_16bit<T, DP, NW, OCC>, grid, 64 * NW, a, stream);
   FA_CASE(32) FA_CASE(64) FA_CASE(80) FA_CASE(96) FA_CASE(128) FA_CASE(160) FA_CASE(192)
   FA_CASE(256)
 #undef FA_CASE

@@ -131,7 +131,33 @@ constexpr int pad_to_residue(int min_bytes, int residue) {
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit inputs (bf16 / f16).  D = head_dim rounded up to 16, NW waves.
+// Buffer-resource helpers.  A raw buffer load whose byte offset lies at or
+// beyond num_records returns zeros without touching memory, which gives
+// branch-free zero padding of ragged tiles; a store there is dropped.
+// ---------------------------------------------------------------------------
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit dword access, no swizzle
+constexpr uint32_t kOutOfRange = 0xFFFFFF00u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes,
+                                           kBufferFlags);
+}
+
+__device__ inline float xlane_max(float x) {  // max with lane l ^ 32
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+__device__ inline float xlane_sum(float x) {  // sum with lane l ^ 32
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit inputs (bf16 / f16).  D = head_dim rounded up to 16, NW waves per
+// workgroup, OCC waves per SIMD targeted by the register allocator.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW>
 struct Tile16 {
@@ -140,36 +166,43 @@ struct Tile16 {
   static constexpr int NT = 64 * NW;           // threads per workgroup
   static constexpr int KSTEPS = D / 16;        // k-steps of the S^T MFMA (16 dims each)
   static constexpr int DBLK = (D + 31) / 32;   // 32-dim blocks of the O^T accumulator
-  static constexpr int CH = D / 8;             // 16-byte chunks per row
   // K rows: stride = 16 (mod 256) bytes, so the 32 lanes reading one 16-byte
   // chunk of 32 consecutive rows fall on distinct bank groups.
   static constexpr int KROW = D * 2 + 16;
   // V rows: stride = 64 (mod 256) bytes, so the 4 rows x 32 bytes gathered by
   // each 16-lane group of a transposing read fall on distinct banks.
   static constexpr int VROW = pad_to_residue(DBLK * 64, 64);
+  static constexpr int KSLOTS = KROW / 16;     // 16-byte LDS slots per K row (incl. padding)
+  static constexpr int VSLOTS = VROW / 16;
+  static constexpr int KINSTR = BN * KSLOTS / 64;  // wave-wide 1 KiB loads per K tile
+  static constexpr int VINSTR = BN * VSLOTS / 64;
+  static constexpr int KPER = (KINSTR + NW - 1) / NW;  // per wave
+  static constexpr int VPER = (VINSTR + NW - 1) / NW;
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = BN * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int LOADS = (BN * CH + NT - 1) / NT;  // 16-byte chunks per thread per tensor
   static_assert(D % 16 == 0 && D <= 256, "head_dim padding");
   static_assert(KROW % 16 == 0 && VROW % 16 == 0, "16-byte aligned rows");
+  static_assert((BN * KSLOTS) % 64 == 0 && (BN * VSLOTS) % 64 == 0, "whole wave loads");
 };
 
+// Body of the 16-bit kernel; the __global__ entry points that instantiate it
+// (with their occupancy attributes) are defined next to the launcher.
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
+__device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   using G = Tile16<T, D, NW>;
   using M = Mfma<T>;
   typedef typename M::frag frag;
-  constexpr int BN = G::BN, NT = G::NT, CH = G::CH, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
+  constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
   constexpr int KROW = G::KROW, VROW = G::VROW;
 
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
   FA_LDS char* lds = (FA_LDS char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;   // query column owned by this lane
   const int hi = lane >> 5;    // which half of the 32x32 result rows
 
@@ -187,6 +220,7 @@ __global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
   const int my_q = qw + l32;            // query row of this lane
   const int wave_last = min(qw + 31, a.seq_q - 1);
   const bool wave_live = qw < a.seq_q;
+  const int wave_rows = wave_live ? min(32, a.seq_q - qw) : 0;
 
   // keys this workgroup must visit (causal: up to its last real query)
   const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + G::BM)) : a.seq_k;
@@ -194,50 +228,53 @@ __global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
 
   // ---- resident Q fragment: B operand of S^T, lane = (query l32, dims 8*hi..+7 of each step)
   frag qf[KSTEPS];
+  {
+    const int32_t nrec = wave_rows > 0 ? (wave_rows - 1) * (int32_t)a.q_ss * 2 + a.head_dim * 2 : 0;
+    const auto rq = make_rsrc(qg + (int64_t)(wave_live ? qw : 0) * a.q_ss, nrec);
+    const uint32_t sign = a.neg_scale ? 0x80008000u : 0u;
 #pragma unroll
-  for (int st = 0; st < KSTEPS; ++st) {
-    const int col = st * 16 + hi * 8;
-    u32x4_t raw = {0u, 0u, 0u, 0u};
-    if (my_q < a.seq_q && col < a.head_dim)
-      raw = *(const u32x4_t*)(qg + (int64_t)my_q * a.q_ss + col);
-    if (a.neg_scale) raw ^= (u32x4_t){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-    qf[st] = __builtin_bit_cast(frag, raw);
+    for (int st = 0; st < KSTEPS; ++st) {
+      const int col = st * 16 + hi * 8;
+      const uint32_t off = col < a.head_dim ? (uint32_t)(l32 * (int32_t)a.q_ss * 2 + col * 2)
+                                            : kOutOfRange;
+      u32x4_t raw = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      raw ^= (u32x4_t){sign, sign, sign, sign};
+      qf[st] = __builtin_bit_cast(frag, raw);
+    }
   }
 
-  // ---- zero the LDS once (pads and V columns beyond D are read but never written)
-  for (int off = tid * 16; off < G::LDS_BYTES; off += NT * 16)
-    *(FA_LDS u32x4_t*)(lds + off) = (u32x4_t){0u, 0u, 0u, 0u};
-
-  // ---- K/V tile staging through registers
-  u32x4_t kreg[G::LOADS], vreg[G::LOADS];
-  auto load_tile = [&](int t) {
-    const int key0 = t * BN;
+  // ---- per-lane byte offsets of the direct-to-LDS tile loads (tile independent)
+  uint32_t koff[G::KPER], voff[G::VPER];
 #pragma unroll
-    for (int n = 0; n < G::LOADS; ++n) {
-      const int ci = tid + n * NT;
-      const int row = ci / CH, c = ci - (ci / CH) * CH;
-      const bool ok = (ci < BN * CH) && (key0 + row < a.seq_k) && (c * 8 < a.head_dim);
-      u32x4_t kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
-      if (ok) {
-        kz = *(const u32x4_t*)(kg + (int64_t)(key0 + row) * a.k_ss + c * 8);
-        vz = *(const u32x4_t*)(vg + (int64_t)(key0 + row) * a.v_ss + c * 8);
-      }
-      kreg[n] = kz;
-      vreg[n] = vz;
-    }
-  };
-  auto store_tile = [&](int stage) {
+  for (int n = 0; n < G::KPER; ++n) {
+    const int slot = (wave + NW * n) * 64 + lane;
+    const int row = slot / G::KSLOTS, ch = slot - (slot / G::KSLOTS) * G::KSLOTS;
+    koff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.k_ss * 2 + ch * 16) : kOutOfRange;
+  }
+#pragma unroll
+  for (int n = 0; n < G::VPER; ++n) {
+    const int slot = (wave + NW * n) * 64 + lane;
+    const int row = slot / G::VSLOTS, ch = slot - (slot / G::VSLOTS) * G::VSLOTS;
+    voff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
+  }
+  // K and V tile t -> LDS stage; rows >= seq_k and dims >= head_dim land as zeros
+  auto issue_tile = [&](int t, int stage) {
+    const int key0 = t * BN;
+    const int rows = min(BN, a.seq_k - key0);
+    const auto rk = make_rsrc(kg + (int64_t)key0 * a.k_ss, (rows - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2);
+    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
     FA_LDS char* kb = lds + stage * G::STAGE;
     FA_LDS char* vb = kb + G::KBYTES;
 #pragma unroll
-    for (int n = 0; n < G::LOADS; ++n) {
-      const int ci = tid + n * NT;
-      if (ci < BN * CH) {
-        const int row = ci / CH, c = ci - (ci / CH) * CH;
-        *(FA_LDS u32x4_t*)(kb + row * KROW + c * 16) = kreg[n];
-        *(FA_LDS u32x4_t*)(vb + row * VROW + c * 16) = vreg[n];
-      }
-    }
+    for (int n = 0; n < G::KPER; ++n)
+      if (wave + NW * n < G::KINSTR)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(kb + (wave + NW * n) * 1024), 16,
+                                                 koff[n], 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < G::VPER; ++n)
+      if (wave + NW * n < G::VINSTR)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(vb + (wave + NW * n) * 1024), 16,
+                                                 voff[n], 0, 0, 0);
   };
 
   // ---- online-softmax state (per lane: query l32; both halves agree on m)
@@ -248,18 +285,17 @@ __global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
   float l_run = 0.f;        // partial row sum over this lane's keys
   const float c = a.c;
 
-  // lane-constant LDS offsets
+  // lane-constant LDS offsets of the MFMA operand reads
   const int k_lane = l32 * KROW + hi * 16;
   const int s16 = lane & 15;
   const int v_lane = (4 * hi + (s16 >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
 
-  if (n_tiles > 0) load_tile(0);
-  __syncthreads();  // zero-fill complete before the first tile lands
-  if (n_tiles > 0) store_tile(0);
+  if (n_tiles > 0) issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
     const int key0 = t * BN;
     const bool skip = !wave_live || (a.causal && key0 > wave_last);
     if (!skip) {
@@ -294,16 +330,14 @@ __global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
       }
 
       // row max: in-lane over 32 keys, then with the partner half
-      float mx = s[0][0];
+      float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      mx = xlane_max(mx);
       const float m_tile = mx * c;  // c > 0, so max(s) * c = max(s * c)
       const float m_new = fmaxf(m_run, m_tile);
       const bool upd = m_new > m_run + kRescaleLog2;
-      if (__ballot(upd)) {
+      if (__builtin_amdgcn_ballot_w64(upd)) {
         const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
         l_run *= alpha;
 #pragma unroll
@@ -314,17 +348,18 @@ __global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
 
       // P = exp2(s*c - m), partial row sums, pack to the input type
       uint32_t pk[2][8];
-      float lsum = 0.f;
+      float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
-          lsum += p0 + p1;
+          lsum0 += p0;
+          lsum1 += p1;
           pk[kb2][r >> 1] = M::pack2(p0, p1);
         }
-      l_run += lsum;
+      l_run += lsum0 + lsum1;
 
       // O^T += V^T P^T: four 16-key MFMA steps per 32-dim block
 #pragma unroll
@@ -344,30 +379,29 @@ __global__ __launch_bounds__(64 * NW) void fa_fwd_16bit(FwdArgs a) {
         }
       }
     }
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
+    __syncthreads();                // ... and everyone's; stage t is free again
   }
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
   if (!wave_live) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (my_q < a.seq_q) {
-    const float inv = 1.0f / l_tot;
-    T* orow = og + (int64_t)my_q * a.o_ss;
+  const float l_tot = xlane_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  const int32_t onrec = (wave_rows - 1) * (int32_t)a.o_ss * 2 + a.head_dim * 2;
+  const auto ro = make_rsrc(og + (int64_t)qw * a.o_ss, onrec);
+  const uint32_t orow = (uint32_t)(l32 * (int32_t)a.o_ss * 2);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+  for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * hi;
-        if (d0 < a.head_dim) {
-          const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
-                             M::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-          *(u32x2_t*)(orow + d0) = w;
-        }
-      }
-    if (hi == 0 && a.lse != nullptr)
-      a.lse[(int64_t)bh * a.seq_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
-  }
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + 8 * g + 4 * hi;
+      const uint32_t off = (d0 < a.head_dim && l32 < wave_rows) ? orow + d0 * 2 : kOutOfRange;
+      const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                         M::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+    }
+  if (hi == 0 && a.lse != nullptr && my_q < a.seq_q)
+    a.lse[(int64_t)bh * a.seq_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
