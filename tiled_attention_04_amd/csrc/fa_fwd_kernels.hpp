@@ -146,7 +146,7 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t num
 __device__ inline float xlane_max(float x) {  // max with lane l ^ 32
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                    false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
 __device__ inline float xlane_sum(float x) {  // sum with lane l ^ 32
@@ -297,8 +297,10 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   for (int t = 0; t < n_tiles; ++t) {
     if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
     const int key0 = t * BN;
-    const bool skip = !wave_live || (a.causal && key0 > wave_last);
-    if (!skip) {
+    // Every wave computes every tile of the workgroup: on the few diagonal
+    // tiles that lie wholly above a wave's rows the causal mask zeroes P, and
+    // a uniform control flow keeps the accumulators in place across tiles.
+    {
       FA_LDS char* kb = lds + (t & 1) * G::STAGE;
       FA_LDS char* vb = kb + G::KBYTES;
 
@@ -330,12 +332,12 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
       }
 
       // row max: in-lane over 32 keys, then with the partner half
-      float mx = fmaxf(s[0][0], s[1][0]);
+      float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[0][r], s[1][r]));
       mx = xlane_max(mx);
       const float m_tile = mx * c;  // c > 0, so max(s) * c = max(s * c)
-      const float m_new = fmaxf(m_run, m_tile);
+      const float m_new = __builtin_elementwise_maximum(m_run, m_tile);
       const bool upd = m_new > m_run + kRescaleLog2;
       if (__builtin_amdgcn_ballot_w64(upd)) {
         const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
