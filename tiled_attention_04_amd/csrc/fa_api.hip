@@ -59,9 +59,6 @@ fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& 
 }
 
 // Instantiated head-dim paddings: the smallest one >= head_dim is used.
-#ifndef FA_NW16
-#define FA_NW16 4  // waves per workgroup (32 query rows each)
-#endif
 #ifndef FA_OCC16
 #define FA_OCC16 2  // waves per SIMD the register budget is sized for
 #endif
@@ -72,9 +69,12 @@ void fa_fwd_16bit(fa::FwdArgs a) {
   fa::fa_fwd_16bit_body<T, D, NW>(a);
 }
 
-template <typename T>
-fa_status_t launch_16bit(fa::FwdArgs& a, int64_t head_dim, void* stream) {
-  constexpr int NW = FA_NW16, OCC = FA_OCC16;
+// Workgroups of 8 waves (256 query rows) halve the K/V traffic per query and
+// run two waves per SIMD from one workgroup; 4-wave workgroups (128 rows) are
+// used when the 8-wave grid would be too small to fill the 256 CUs well.
+template <typename T, int NW>
+fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
+  constexpr int OCC = FA_OCC16;
   a.n_qtiles = (int32_t)((a.seq_q + 32 * NW - 1) / (32 * NW));
   const int64_t grid = (int64_t)a.n_bh * a.n_qtiles;
   if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
@@ -85,6 +85,17 @@ fa_status_t launch_16bit(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   FA_CASE(256)
 #undef FA_CASE
   return fail(FA_ERR_HEAD_DIM, "head_dim %lld unsupported", (long long)head_dim);
+}
+
+template <typename T>
+fa_status_t launch_16bit(fa::FwdArgs& a, int64_t head_dim, void* stream) {
+#ifdef FA_FORCE_NW16
+  return launch_16bit_nw<T, FA_FORCE_NW16>(a, head_dim, stream);
+#else
+  const int64_t wg8 = (int64_t)a.n_bh * ((a.seq_q + 255) / 256);
+  if (wg8 >= 1024) return launch_16bit_nw<T, 8>(a, head_dim, stream);
+  return launch_16bit_nw<T, 4>(a, head_dim, stream);
+#endif
 }
 
 fa_status_t launch_f32(fa::FwdArgs& a, int64_t head_dim, void* stream) {

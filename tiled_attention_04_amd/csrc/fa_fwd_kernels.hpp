@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -257,19 +259,24 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     const int row = slot / G::VSLOTS, ch = slot - (slot / G::VSLOTS) * G::VSLOTS;
     voff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
   }
-  // K and V tile t -> LDS stage; rows >= seq_k and dims >= head_dim land as zeros
-  auto issue_tile = [&](int t, int stage) {
-    const int key0 = t * BN;
+  // Tile j's K goes to the K area and its V to the V area of LDS stage j & 1;
+  // rows >= seq_k and dims >= head_dim land as zeros.
+  auto issue_k = [&](int j) {
+    const int key0 = j * BN;
     const int rows = min(BN, a.seq_k - key0);
     const auto rk = make_rsrc(kg + (int64_t)key0 * a.k_ss, (rows - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2);
-    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
-    FA_LDS char* kb = lds + stage * G::STAGE;
-    FA_LDS char* vb = kb + G::KBYTES;
+    FA_LDS char* kb = lds + (j & 1) * G::STAGE;
 #pragma unroll
     for (int n = 0; n < G::KPER; ++n)
       if (wave + NW * n < G::KINSTR)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(kb + (wave + NW * n) * 1024), 16,
                                                  koff[n], 0, 0, 0);
+  };
+  auto issue_v = [&](int j) {
+    const int key0 = j * BN;
+    const int rows = min(BN, a.seq_k - key0);
+    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
+    FA_LDS char* vb = lds + (j & 1) * G::STAGE + G::KBYTES;
 #pragma unroll
     for (int n = 0; n < G::VPER; ++n)
       if (wave + NW * n < G::VINSTR)
@@ -290,99 +297,132 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   const int s16 = lane & 15;
   const int v_lane = (4 * hi + (s16 >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
 
-  if (n_tiles > 0) issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
-    const int key0 = t * BN;
-    // Every wave computes every tile of the workgroup: on the few diagonal
-    // tiles that lie wholly above a wave's rows the causal mask zeroes P, and
-    // a uniform control flow keeps the accumulators in place across tiles.
-    {
-      FA_LDS char* kb = lds + (t & 1) * G::STAGE;
-      FA_LDS char* vb = kb + G::KBYTES;
-
-      // S^T = K Q^T for two 32-key blocks
-      f32x16_t s[2];
+  // S^T = K Q^T for the two 32-key blocks of the K tile in stage P
+  auto scores = [&](auto parity, f32x16_t (&s)[2]) {
+    FA_LDS char* kb = lds + decltype(parity)::value * G::STAGE;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = (f32x16_t){};
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        f32x16_t sc = (f32x16_t){};
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-          const frag kf = __builtin_bit_cast(
-              frag, *(FA_LDS u32x4_t*)(kb + k_lane + kb2 * 32 * KROW + st * 32));
-          sc = M::mma(kf, qf[st], sc);
-        }
-        s[kb2] = sc;
+        const frag kf = __builtin_bit_cast(
+            frag, *(FA_LDS u32x4_t*)(kb + k_lane + kb2 * 32 * KROW + st * 32));
+        s[kb2] = M::mma(kf, qf[st], s[kb2]);
       }
+  };
 
-      // masks: key tail and causal diagonal (only on tiles that need them)
-      const bool need_mask = (key0 + BN > a.seq_k) || (a.causal && key0 + BN - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool vis = key < a.seq_k && (!a.causal || key <= my_q);
-            s[kb2][r] = vis ? s[kb2][r] : -INFINITY;
-          }
-      }
-
-      // row max: in-lane over 32 keys, then with the partner half
-      float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[0][r], s[1][r]));
-      mx = xlane_max(mx);
-      const float m_tile = mx * c;  // c > 0, so max(s) * c = max(s * c)
-      const float m_new = __builtin_elementwise_maximum(m_run, m_tile);
-      const bool upd = m_new > m_run + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(upd)) {
-        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
-        m_run = upd ? m_new : m_run;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-
-      // P = exp2(s*c - m), partial row sums, pack to the input type
-      uint32_t pk[2][8];
-      float lsum0 = 0.f, lsum1 = 0.f;
+  // masks (key tail, causal diagonal), row max and the lazy rescale for tile t
+  auto stats = [&](int t, f32x16_t (&s)[2]) {
+    const int key0 = t * BN;
+    const bool need_mask = (key0 + BN > a.seq_k) || (a.causal && key0 + BN - 1 > qw);
+    if (need_mask) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
-          lsum0 += p0;
-          lsum1 += p1;
-          pk[kb2][r >> 1] = M::pack2(p0, p1);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool vis = key < a.seq_k && (!a.causal || key <= my_q);
+          s[kb2][r] = vis ? s[kb2][r] : -INFINITY;
         }
-      l_run += lsum0 + lsum1;
+    }
+    float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[0][r], s[1][r]));
+    mx = xlane_max(mx);
+    const float m_tile = mx * c;  // c > 0, so max(s) * c = max(s * c)
+    const float m_new = __builtin_elementwise_maximum(m_run, m_tile);
+    const bool upd = m_new > m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
+      m_run = upd ? m_new : m_run;
+    }
+  };
 
-      // O^T += V^T P^T: four 16-key MFMA steps per 32-dim block
+  // P = exp2(s*c - m) rounded to the input type, and its partial row sum
+  auto probs = [&](const f32x16_t (&s)[2], uint32_t (&pk)[2][8]) {
+    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+    float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const u32x4_t praw = {pk[u >> 1][4 * (u & 1) + 0], pk[u >> 1][4 * (u & 1) + 1],
-                              pk[u >> 1][4 * (u & 1) + 2], pk[u >> 1][4 * (u & 1) + 3]};
-        const frag pf = __builtin_bit_cast(frag, praw);
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          FA_LDS char* p0 = vb + v_lane + (16 * u) * VROW + db * 64;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p0);
-          const i16x4_t up =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + 8 * VROW));
-          const u32x4_t vraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                                __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
-          acc[db] = M::mma(__builtin_bit_cast(frag, vraw), pf, acc[db]);
-        }
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
+        lsum0 += p0;
+        lsum1 += p1;
+        pk[kb2][r >> 1] = M::pack2(p0, p1);
+      }
+    l_run += lsum0 + lsum1;
+  };
+
+  // O^T += V^T P^T with the V tile in stage P: four 16-key steps per 32-dim block
+  auto pv = [&](auto parity, const uint32_t (&pk)[2][8]) {
+    FA_LDS char* vb = lds + decltype(parity)::value * G::STAGE + G::KBYTES;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4_t praw = {pk[u >> 1][4 * (u & 1) + 0], pk[u >> 1][4 * (u & 1) + 1],
+                            pk[u >> 1][4 * (u & 1) + 2], pk[u >> 1][4 * (u & 1) + 3]};
+      const frag pf = __builtin_bit_cast(frag, praw);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        FA_LDS char* p0 = vb + v_lane + (16 * u) * VROW + db * 64;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p0);
+        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + 8 * VROW));
+        const u32x4_t vraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                              __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
+        acc[db] = M::mma(__builtin_bit_cast(frag, vraw), pf, acc[db]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
-    __syncthreads();                // ... and everyone's; stage t is free again
+  };
+
+  // One pipelined step for tile t (parity = t & 1, known at compile time):
+  // the MFMAs of S(t+1) are issued in the same basic block as the softmax
+  // VALU work of tile t, so the matrix pipe stays busy while P(t) is formed;
+  // then P(t) V(t).  K runs one tile ahead of V in LDS: during step t the
+  // loads of K(t+2) and V(t+1) are in flight.
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  auto step = [&](int t, auto parity, auto has_next, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    constexpr int P = decltype(parity)::value;
+    using Next = std::integral_constant<int, 1 - P>;
+    stats(t, cur);
+    if (t + 2 < n_tiles) issue_k(t + 2);
+    if (t + 1 < n_tiles) issue_v(t + 1);
+    uint32_t pk[2][8];
+    if constexpr (decltype(has_next)::value) scores(Next{}, nxt);
+    probs(cur, pk);
+    pv(parity, pk);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+2) / V(t+1) loads have landed
+    __syncthreads();                // ... and everyone's; the areas read in step t are free
+  };
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+
+  f32x16_t sa[2], sb[2];
+  if (n_tiles > 0) {
+    issue_k(0);
+    issue_v(0);
+    if (n_tiles > 1) issue_k(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    scores(Even{}, sa);
+    __syncthreads();  // K(0) consumed by all waves before step 0 loads K(2) over it
+    int t = 0;
+    for (; t + 2 < n_tiles; t += 2) {
+      step(t, Even{}, Yes{}, sa, sb);
+      step(t + 1, Odd{}, Yes{}, sb, sa);
+    }
+    if (t + 1 < n_tiles) {
+      step(t, Even{}, Yes{}, sa, sb);
+      step(t + 1, Odd{}, No{}, sb, sa);
+    } else {
+      step(t, Even{}, No{}, sa, sb);
+    }
   }
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
