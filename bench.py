@@ -65,37 +65,47 @@ def load_traffic():
 
 
 def cpu_baseline(inp, target_s=15.0):
-    """Time the C oracle on a bounded sample of rows of the workload."""
+    """Time the C oracle on a bounded sample of query rows of the workload.
+
+    A 64-row pilot sizes the sample to about target_s seconds; the rows are
+    evenly spaced over the first few (batch, head) pairs, so their causal
+    lengths average like the full workload's."""
     import numpy as np
     import oracle
 
     w = inp.workload
-    heads = [(0, 0)]
-    q64 = inp.as_bhsd_f64("q", heads)
-    k64 = inp.as_bhsd_f64("k", heads)
-    v64 = inp.as_bhsd_f64("v", heads)
     S = w.seq_q
 
     def row_flops(rows):
-        keys = np.minimum(rows + 1, w.seq_k) if w.causal else np.full(rows.shape, w.seq_k)
+        i = rows % S
+        keys = np.minimum(i + 1, w.seq_k) if w.causal else np.full(rows.shape, w.seq_k)
         return float(np.sum(4.0 * keys * w.head_dim))
 
-    def pick(n):  # evenly spaced rows: their mean causal length matches the workload's
-        return np.unique(np.linspace(0, S - 1, n).astype(np.int64))
+    def run(n_heads, n_rows):
+        heads = [(bh // w.heads, bh % w.heads) for bh in range(n_heads)]
+        q64 = inp.as_bhsd_f64("q", heads)
+        k64 = inp.as_bhsd_f64("k", heads)
+        v64 = inp.as_bhsd_f64("v", heads)
+        rows = np.unique(np.linspace(0, n_heads * S - 1, n_rows).astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=rows)
+        return rows, time.perf_counter() - t0
 
-    pilot = pick(64)
-    t0 = time.perf_counter()
-    oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=pilot)
-    t_pilot = max(time.perf_counter() - t0, 1e-3)
-    n = int(min(S, max(64, 64 * target_s / t_pilot)))
-    rows = pick(n)
-    t0 = time.perf_counter()
-    oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=rows)
-    dt = time.perf_counter() - t0
+    mean_row = 4.0 * w.head_dim * ((w.seq_k + 1) / 2 if w.causal else w.seq_k)
+    max_rows = w.batch * w.heads * S
+    n_rows = 256
+    for _ in range(4):  # grow the sample until it takes a sizeable share of target_s
+        n_heads = int(min(w.batch * w.heads, max(1, -(-n_rows // S))))
+        rows, dt = run(n_heads, min(n_rows, n_heads * S))
+        if dt >= 0.4 * target_s or rows.size >= max_rows:
+            break
+        rate = row_flops(rows) / max(dt, 1e-3)  # oracle FLOP/s on this host
+        n_rows = int(min(max_rows, max(2 * n_rows, rate * target_s / mean_row)))
     return {"value": row_flops(rows) / dt / 1e12, "unit": "TFLOP/s",
             "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{rows.size} evenly spaced query rows of head (0,0) of the same workload "
-                      f"(fp64 C oracle, materialised softmax), {dt:.1f} s wall"}
+            "sample": f"{rows.size} evenly spaced query rows of the first {n_heads} (batch, head) "
+                      f"pairs of the same workload (fp64 C oracle, materialised softmax), "
+                      f"{dt:.1f} s wall"}
 
 
 def summarize_pmc(d):

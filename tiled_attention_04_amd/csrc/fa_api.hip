@@ -81,8 +81,16 @@ fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
 #define FA_CASE(DP)                                                            \
   if (head_dim <= DP) return launch(fa_fwd_16bit<T, DP, NW, OCC>, grid, 64 * NW, a, stream);
-  FA_CASE(32) FA_CASE(64) FA_CASE(80) FA_CASE(96) FA_CASE(128) FA_CASE(160) FA_CASE(192)
-  FA_CASE(256)
+  FA_CASE(32) FA_CASE(64) FA_CASE(80) FA_CASE(96) FA_CASE(128)
+#undef FA_CASE
+  // head_dim > 128 does not fit two waves per SIMD: 4-wave workgroups, one wave per SIMD
+#define FA_CASE(DP)                                                            \
+  if (head_dim <= DP) return launch(fa_fwd_16bit<T, DP, 4, 1>, grid4, 256, a4, stream);
+  fa::FwdArgs a4 = a;
+  a4.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
+  const int64_t grid4 = (int64_t)a.n_bh * a4.n_qtiles;
+  if (grid4 > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid4);
+  FA_CASE(160) FA_CASE(192) FA_CASE(256)
 #undef FA_CASE
   return fail(FA_ERR_HEAD_DIM, "head_dim %lld unsupported", (long long)head_dim);
 }

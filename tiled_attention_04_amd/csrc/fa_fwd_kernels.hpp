@@ -58,6 +58,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (P <= 256)
 
+
+
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -298,8 +301,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   const int v_lane = (4 * hi + (s16 >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
 
   // S^T = K Q^T for the two 32-key blocks of the K tile in stage P
-  auto scores = [&](auto parity, f32x16_t (&s)[2]) {
-    FA_LDS char* kb = lds + decltype(parity)::value * G::STAGE;
+  auto scores = [&](int parity, f32x16_t (&s)[2]) {
+    FA_LDS char* kb = lds + parity * G::STAGE;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = (f32x16_t){};
 #pragma unroll
@@ -361,8 +364,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   };
 
   // O^T += V^T P^T with the V tile in stage P: four 16-key steps per 32-dim block
-  auto pv = [&](auto parity, const uint32_t (&pk)[2][8]) {
-    FA_LDS char* vb = lds + decltype(parity)::value * G::STAGE + G::KBYTES;
+  auto pv = [&](int parity, const uint32_t (&pk)[2][8]) {
+    FA_LDS char* vb = lds + parity * G::STAGE + G::KBYTES;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const u32x4_t praw = {pk[u >> 1][4 * (u & 1) + 0], pk[u >> 1][4 * (u & 1) + 1],
@@ -389,14 +392,13 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   using Odd = std::integral_constant<int, 1>;
   auto step = [&](int t, auto parity, auto has_next, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     constexpr int P = decltype(parity)::value;
-    using Next = std::integral_constant<int, 1 - P>;
     stats(t, cur);
     if (t + 2 < n_tiles) issue_k(t + 2);
     if (t + 1 < n_tiles) issue_v(t + 1);
     uint32_t pk[2][8];
-    if constexpr (decltype(has_next)::value) scores(Next{}, nxt);
+    if constexpr (decltype(has_next)::value) scores(1 - P, nxt);
     probs(cur, pk);
-    pv(parity, pk);
+    pv(P, pk);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+2) / V(t+1) loads have landed
     __syncthreads();                // ... and everyone's; the areas read in step t are free
   };
@@ -410,7 +412,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     if (n_tiles > 1) issue_k(1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    scores(Even{}, sa);
+    scores(0, sa);
     __syncthreads();  // K(0) consumed by all waves before step 0 loads K(2) over it
     int t = 0;
     for (; t + 2 < n_tiles; t += 2) {
