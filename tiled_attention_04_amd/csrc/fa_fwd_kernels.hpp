@@ -160,6 +160,25 @@ __device__ inline float xlane_sum(float x) {  // sum with lane l ^ 32
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// Maximum of the 32 values of two 16-register score blocks as a depth-4 tree
+// of v_maximum3_f32 (a linear chain would be 16 dependent instructions).
+__device__ inline float row_max32(const f32x16_t& a, const f32x16_t& b) {
+  float t[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i)
+    t[i] = __builtin_elementwise_maximum(a[3 * i], __builtin_elementwise_maximum(a[3 * i + 1], a[3 * i + 2]));
+#pragma unroll
+  for (int i = 0; i < 5; ++i)
+    t[5 + i] = __builtin_elementwise_maximum(b[3 * i], __builtin_elementwise_maximum(b[3 * i + 1], b[3 * i + 2]));
+  t[10] = __builtin_elementwise_maximum(a[15], b[15]);
+  const float u0 = __builtin_elementwise_maximum(t[0], __builtin_elementwise_maximum(t[1], t[2]));
+  const float u1 = __builtin_elementwise_maximum(t[3], __builtin_elementwise_maximum(t[4], t[5]));
+  const float u2 = __builtin_elementwise_maximum(t[6], __builtin_elementwise_maximum(t[7], t[8]));
+  const float u3 = __builtin_elementwise_maximum(t[9], t[10]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(u0, u1),
+                                       __builtin_elementwise_maximum(u2, u3));
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit inputs (bf16 / f16).  D = head_dim rounded up to 16, NW waves per
 // workgroup, OCC waves per SIMD targeted by the register allocator.
@@ -329,10 +348,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
           s[kb2][r] = vis ? s[kb2][r] : -INFINITY;
         }
     }
-    float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r)
-      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[0][r], s[1][r]));
+    float mx = row_max32(s[0], s[1]);
     mx = xlane_max(mx);
     const float m_tile = mx * c;  // c > 0, so max(s) * c = max(s * c)
     const float m_new = __builtin_elementwise_maximum(m_run, m_tile);
@@ -349,18 +365,17 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   // P = exp2(s*c - m) rounded to the input type, and its partial row sum
   auto probs = [&](const f32x16_t (&s)[2], uint32_t (&pk)[2][8]) {
     const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-    float lsum0 = 0.f, lsum1 = 0.f;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};  // four short add chains instead of one long one
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
         const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
-        lsum0 += p0;
-        lsum1 += p1;
+        part[(r >> 1) & 3] += p0 + p1;
         pk[kb2][r >> 1] = M::pack2(p0, p1);
       }
-    l_run += lsum0 + lsum1;
+    l_run += (part[0] + part[1]) + (part[2] + part[3]);
   };
 
   // O^T += V^T P^T with the V tile in stage P: four 16-key steps per 32-dim block
