@@ -1,4 +1,4 @@
-"""NumPy float64 oracle for the fused attention forward.
+"""NumPy float64 oracle for the fused attention forward and its gradients.
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke entry point
 and the benchmark's CPU-baseline leg, never by the HIP library or its binding.
@@ -48,3 +48,40 @@ def attention_forward(q, k, v, sm_scale, causal, row_block=256):
                 o[b, h, rows] = (unnorm / denom) @ v[b, h]
                 lse[b, h, rows] = row_max[:, 0] + np.log(denom[:, 0])
     return o, lse
+
+
+def attention_backward(q, k, v, dout, sm_scale, causal):
+    """Gradients dQ, dK, dV of O = attention(q, k, v) for upstream dout.
+
+    Materialised per (batch, head), float64.  Follows "[CS336] Assignment 2:
+    Systems", section "FlashAttention V2": dV = P^T dO, dP = dO V^T,
+    dS = P o (dP - rowsum(dO o O)), dQ = scale dS K, dK = scale dS^T Q, with
+    P the row softmax of the scaled, masked scores.  Written apart from
+    fa_oracle_bwd.c.  Returns (dq, dk, dv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    visible = np.ones((Sq, Sk), dtype=bool)
+    if causal:
+        visible = np.arange(Sk)[None, :] <= np.arange(Sq)[:, None]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            s = sm_scale * (q[b, h] @ k[b, h].T)
+            s = np.where(visible, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            o = p @ v[b, h]
+            dv[b, h] = p.T @ dout[b, h]
+            dp = dout[b, h] @ v[b, h].T
+            ds = p * (dp - np.sum(dout[b, h] * o, axis=1, keepdims=True))
+            dq[b, h] = sm_scale * (ds @ k[b, h])
+            dk[b, h] = sm_scale * (ds.T @ q[b, h])
+    return dq, dk, dv
