@@ -19,6 +19,10 @@ Other modes:
   --copy-calib          also run a plain device copy of 1 GiB (for counter
                         calibration under rocprofv3 --pmc)
   --summarize-pmc DIR   reduce rocprofv3 --pmc output under DIR to a summary
+  --pass bwd            time the backward (fa_bwd: delta, dQ and dK/dV launches)
+                        on the same workload instead; FLOPs counted as 2.5x the
+                        forward's (the five products of the backward), so the
+                        recomputation of P in both phases is extra work
 """
 import argparse
 import glob
@@ -127,6 +131,52 @@ def summarize_pmc(d):
     return res
 
 
+def bench_bwd(args, w, inp, up, q, k, v, o, lse, layout, stream):
+    """Time fa_bwd on the workload (inputs, O, lse and dO resident before timing)."""
+    import torch
+    import tiled_attention_04_amd as fa
+    from tiled_attention_04_amd import synth
+
+    fa.forward(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout, out=o, lse=lse)
+    do = up(synth.make_dout(w))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+
+    def step():
+        fa.backward(q, k, v, o, do, lse, causal=w.causal, sm_scale=w.sm_scale, layout=layout,
+                    dq=dq, dk=dk, dv=dv, delta=delta)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s0, s1 in ev:
+        s0.record(stream)
+        step()
+        s1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = sum(per) / len(per)
+    flops = 2.5 * w.flops()
+    value = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] bwd {args.steps} steps: avg {ms:.4f} ms, median {per[len(per) // 2]:.4f}, "
+          f"min {per[0]:.4f}", file=sys.stderr, flush=True)
+    out = {"metric": "attention bwd TFLOP/s (2.5x forward FLOPs) and % of MI355X bf16 MFMA peak",
+           "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "pass": "bwd", "flops_per_step": flops},
+           "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+           "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "kernel_ms_avg": round(ms, 5),
+                        "kernel_ms_min": round(per[0], 5)}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +186,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-pmc", default=None)
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -174,6 +225,9 @@ def main():
 
     def step():
         fa.forward(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout, out=o, lse=lse)
+
+    if args.which == "bwd":
+        return bench_bwd(args, w, inp, up, q, k, v, o, lse, layout, stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -1,6 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) fused attention forward library
- *         (libfa_mi355x.so).
+ * fa.h -- C ABI of the MI355X (gfx950) fused attention library
+ *         (libfa_mi355x.so): forward (fa_fwd) and gradients (fa_bwd).
  *
  * The operation is the FlashAttention-2 style forward pass:
  *     O = softmax(sm_scale * Q K^T [+ causal mask]) V,   lse_i = log sum_j exp(s_ij)
@@ -96,6 +96,52 @@ typedef struct {
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
                    fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
+                   float sm_scale, int causal, fa_dtype_t dtype, void* stream);
+
+/*
+ * fa_bwd -- enqueue the gradients of fa_fwd on `stream` and return.
+ *
+ * The recomputation form of the FlashAttention-2 backward ("[CS336]
+ * Assignment 2: Systems", section "FlashAttention V2", subsections "High
+ * level" and "Backward Pass"): with L the forward's logsumexp and
+ * D_i = sum_t dout[i,t] o[i,t],
+ *     p_ij = exp(s_ij - L_i) on visible pairs (0 elsewhere),
+ *     dv = P^T dout,  dp = dout V^T,  ds_ij = p_ij (dp_ij - D_i),
+ *     dq = sm_scale * dS K,  dk = sm_scale * dS^T Q,
+ * computed in two phases that each recompute P: one per block of queries
+ * (dq), one per block of keys (dk, dv), plus a first launch that fills delta.
+ *
+ *   q, k, v  the forward's inputs (layouts as for fa_fwd, via q_st/k_st/v_st)
+ *   o        the forward's output  [batch, heads, seq_q, head_dim] via o_st
+ *   dout     gradient of the loss w.r.t. o, same shape as o, via do_st
+ *   lse      the forward's logsumexp, fp32 [batch, heads, seq_q] contiguous
+ *   delta    fp32 [batch, heads, seq_q] contiguous, caller-owned; written
+ *            with D (the call's working vector, readable afterwards)
+ *   dq, dk, dv  outputs, shaped like q, k, v, via dq_st/dk_st/dv_st
+ * All tensors share `dtype`, which must be FA_DTYPE_F16 or FA_DTYPE_BF16;
+ * head_dim must be a multiple of 8 in 1..128.  Accumulation is fp32; P and
+ * dS are rounded to the input type before their products, and the
+ * gradients are rounded to nearest-even into the input type.  Same
+ * visibility rule (causal, top-left) and sm_scale as fa_fwd; lse must come
+ * from fa_fwd (or equal it) for the same q, k, sm_scale and causal.  Keys
+ * that no query sees get zero dk and dv (also when seq_q == 0).
+ *
+ * Ownership: as fa_fwd (caller-owned device memory, no allocation, no
+ * synchronisation).  No output may overlap an input.
+ *
+ * Validation on the host before any HIP call: the fa_fwd rules for sizes,
+ * strides and sm_scale over all eight tensors; dtype FA_DTYPE_F32
+ * -> FA_ERR_DTYPE; head_dim > 128 -> FA_ERR_HEAD_DIM; batch or heads == 0
+ * -> FA_OK with nothing launched; k, v, dk, dv NULL, or (seq_q > 0) q, o,
+ * dout, lse, delta, dq NULL -> FA_ERR_NULL; a tensor not 16-byte aligned or
+ * lse/delta not 4-byte aligned -> FA_ERR_LAYOUT.  If a launch fails
+ * (FA_ERR_HIP) the launches before it in this call stay enqueued.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* dq, void* dk, void* dv,
+                   int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                   fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
+                   fa_strides_t do_st, fa_strides_t dq_st, fa_strides_t dk_st, fa_strides_t dv_st,
                    float sm_scale, int causal, fa_dtype_t dtype, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */

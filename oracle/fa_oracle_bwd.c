@@ -194,7 +194,9 @@ int fa_oracle_bwd_dq_rows(const double* q, const double* k, const double* v, con
 }
 
 /* dK and dV of selected flat key rows ((b*H + h)*Sk + j): dk, dv [n_keys, D].
- * L and D of every query row of the heads involved are computed first. */
+ * L and D of the query rows that see a selected key (every row of its head,
+ * or rows i >= the head's smallest selected key when causal) are computed
+ * first. */
 int fa_oracle_bwd_dkv_rows(const double* q, const double* k, const double* v, const double* dout,
                            const int64_t* keys, int64_t n_keys, double* dk, double* dv,
                            int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
@@ -204,8 +206,8 @@ int fa_oracle_bwd_dkv_rows(const double* q, const double* k, const double* v, co
   const int64_t n_bh = batch * heads;
   for (int64_t r = 0; r < n_keys; ++r)
     if (keys[r] < 0 || keys[r] >= n_bh * seq_k) return -1;
-  /* which heads are needed */
-  char* need = (char*)calloc((size_t)(n_bh > 0 ? n_bh : 1), 1);
+  /* first query row needed per head (seq_q: none) */
+  int64_t* need = (int64_t*)malloc((size_t)(n_bh > 0 ? n_bh : 1) * sizeof(int64_t));
   double* Lall = (double*)malloc((size_t)(n_bh * seq_q + 1) * sizeof(double));
   double* Dall = (double*)malloc((size_t)(n_bh * seq_q + 1) * sizeof(double));
   if (!need || !Lall || !Dall) {
@@ -214,7 +216,11 @@ int fa_oracle_bwd_dkv_rows(const double* q, const double* k, const double* v, co
     free(Dall);
     return -2;
   }
-  for (int64_t r = 0; r < n_keys; ++r) need[keys[r] / seq_k] = 1;
+  for (int64_t bh = 0; bh < n_bh; ++bh) need[bh] = seq_q;
+  for (int64_t r = 0; r < n_keys; ++r) {
+    const int64_t bh = keys[r] / seq_k, first = causal ? keys[r] % seq_k : 0;
+    if (first < need[bh]) need[bh] = first;
+  }
   int failed = 0;
 #pragma omp parallel
   {
@@ -223,7 +229,7 @@ int fa_oracle_bwd_dkv_rows(const double* q, const double* k, const double* v, co
 #pragma omp for schedule(dynamic, 16)
     for (int64_t flat = 0; flat < n_bh * seq_q; ++flat) {
       const int64_t bh = flat / seq_q, i = flat % seq_q;
-      if (!need[bh]) continue;
+      if (i < need[bh]) continue;
       if (!score || !o_row) {
 #pragma omp atomic write
         failed = 1;

@@ -77,3 +77,41 @@ def test_fp32_accepts_unaligned_strides():
     # validation; with a NULL q the call then stops at the pointer check.
     rc = call(q=None, qs=S(0, 0, 65, 1), dtype=F32)
     assert rc == 1
+
+
+def call_bwd(q=P, k=P, v=P, o=P, do=P, lse=P, delta=P, dq=P, dk=P, dv=P, batch=1, heads=2,
+             sq=128, sk=128, d=64, sts=None, scale=0.125, causal=0, dtype=BF16):
+    st = dict(q=CONTIG, k=CONTIG, v=CONTIG, o=CONTIG, do=CONTIG, dq=CONTIG, dk=CONTIG, dv=CONTIG)
+    st.update(sts or {})
+    return fa.fa_bwd(q, k, v, o, do, lse, delta, dq, dk, dv, batch, heads, sq, sk, d,
+                     st["q"], st["k"], st["v"], st["o"], st["do"], st["dq"], st["dk"], st["dv"],
+                     scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(batch=-1), 2), (dict(sq=-2), 2), (dict(sk=0), 2), (dict(sq=1 << 31), 2),
+    (dict(dtype=F32), 3), (dict(dtype=5), 3),
+    (dict(d=0), 4), (dict(d=136), 4), (dict(d=256), 4), (dict(d=60), 4),
+    (dict(sts={"do": S(0, 0, 64, 2)}), 5), (dict(sts={"dk": S(0, -64, 64, 1)}), 5),
+    (dict(sts={"dv": S(0, 0, 68, 1)}), 5), (dict(sts={"o": S(0, 0, 1 << 24, 1)}), 5),
+    (dict(dq=P + 8), 5), (dict(do=P + 4), 5), (dict(lse=P + 2), 5), (dict(delta=P + 1), 5),
+    (dict(scale=math.nan), 7),
+    (dict(k=None), 1), (dict(dv=None), 1), (dict(dout_none=True), 1), (dict(lse=None), 1),
+    (dict(delta=None), 1), (dict(dq=None), 1),
+])
+def test_bwd_validation_errors(kwargs, code):
+    if kwargs.pop("dout_none", False):
+        kwargs["do"] = None
+    rc = call_bwd(**kwargs)
+    assert rc == code, (kwargs, rc, fa.last_error())
+    assert fa.last_error() != ""
+
+
+def test_bwd_empty_problem_is_ok_without_pointers():
+    nothing = dict(q=None, k=None, v=None, o=None, do=None, lse=None, delta=None, dq=None,
+                   dk=None, dv=None)
+    for kw in (dict(batch=0), dict(heads=0)):
+        assert call_bwd(**nothing, **kw) == 0
+        assert fa.last_error() == ""
+    # without queries dk and dv are still written (zeros), so they are required
+    assert call_bwd(**nothing, sq=0) == 1

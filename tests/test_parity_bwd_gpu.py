@@ -1,0 +1,188 @@
+"""GPU parity of the backward (fa_bwd) against the CPU gradient oracle.
+
+The HIP path runs fa_fwd then fa_bwd through the C ABI binding on seeded
+synthetic inputs (q, k, v from the workload recipe, dO from its own stream);
+the oracle computes dQ, dK, dV in double from q, k, v and dO alone.
+
+Tolerance (16-bit inputs; the target states none for gradients, so it is
+derived from the arithmetic): every gradient element is an fp32 sum of
+products in which one factor (P or dS) is rounded to the input type
+(relative error <= 2^-9 for bf16 RNE, 2^-11 for fp16), and the result is
+rounded once more; D and P also inherit the rounding of the stored O and the
+fp32 lse.  Relative to the size of the gradient this is a few units of 2^-9,
+so with G = max(1, max|ref|) per tensor we require
+    max |err| <= 2e-2 * G   and   mean |err| <= 2e-3 * G,
+the forward's bounds scaled by the gradient's magnitude.  Any NaN fails.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+from tiled_attention_04_amd import synth  # noqa: E402
+from gpu_cases import device_to_f64, say, to_device  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_MEAN = 2e-2, 2e-3
+
+
+def _layout_of(w):
+    return "shd" if w.layout == "shd" else "bhsd"
+
+
+def _bhsd(x, layout):
+    x = device_to_f64(x)
+    return np.transpose(x, (1, 0, 2))[None] if layout == "shd" else x
+
+
+def run_bwd(w, causal=None, sm_scale=None, inputs=None):
+    """Forward then backward on the GPU; returns inputs (f64 BHSD) and grads (f64 BHSD)."""
+    import torch
+    import tiled_attention_04_amd as fa
+    inp = synth.make_inputs(w) if inputs is None else inputs
+    dout = synth.make_dout(w)
+    causal = w.causal if causal is None else causal
+    scale = w.sm_scale if sm_scale is None else sm_scale
+    layout = _layout_of(w)
+    q, k, v = (to_device(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    do = to_device(dout, w.dtype)
+    o, lse = fa.forward(q, k, v, causal=causal, sm_scale=scale, layout=layout)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=causal, sm_scale=scale, layout=layout)
+    torch.cuda.synchronize()
+    host = {"q": inp.as_bhsd_f64("q"), "k": inp.as_bhsd_f64("k"), "v": inp.as_bhsd_f64("v"),
+            "do": synth.dout_bhsd_f64(w, dout)}
+    grads = {"dq": _bhsd(dq, layout), "dk": _bhsd(dk, layout), "dv": _bhsd(dv, layout)}
+    return host, grads, causal, scale
+
+
+def check(name, gpu, ref, floor=1.0):
+    assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
+    err = np.abs(gpu - ref)
+    g = max(floor, float(np.max(np.abs(ref))))
+    msg = (f"{name}: max {err.max():.3e} mean {err.mean():.3e} (scale {g:.3g}, "
+           f"max|ref| {np.max(np.abs(ref)):.3g})")
+    say(msg)
+    assert err.max() <= TOL_MAX * g, msg
+    assert err.mean() <= TOL_MEAN * g, msg
+
+
+def full_bwd_parity(w, causal=None, sm_scale=None, tag=""):
+    say(f"[gpu] bwd full {w.name} {tag}")
+    host, grads, causal, scale = run_bwd(w, causal, sm_scale)
+    dq, dk, dv, _ = oracle.backward(host["q"], host["k"], host["v"], host["do"], scale, causal)
+    check(f"{w.name}{tag} dq", grads["dq"], dq)
+    check(f"{w.name}{tag} dk", grads["dk"], dk)
+    check(f"{w.name}{tag} dv", grads["dv"], dv)
+    return grads, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("head_dim", [32, 64, 80, 96, 128])
+def test_bwd_ragged(dtype, causal, head_dim):
+    w = synth.custom(f"bwd {dtype} d{head_dim}", dtype, "bhsd", 2, 3, 129, 200, head_dim,
+                     causal=causal, seed=100 + head_dim)
+    full_bwd_parity(w)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_several_blocks(causal):
+    # several dQ query blocks (128) and dK/dV key blocks (256), ragged tails
+    w = synth.custom("bwd bf16 [2,4,700,1100,64]", "bf16", "bhsd", 2, 4, 700, 1100, 64,
+                     causal=causal, seed=7)
+    full_bwd_parity(w)
+
+
+def test_bwd_c3_shape():
+    w = synth.WORKLOADS["c3"]
+    full_bwd_parity(w)
+
+
+def test_bwd_shd_layout_distinct_head_strides():
+    # [seq, heads, d] with seq_q != seq_k: the head strides of q and k differ
+    w = synth.custom("bwd fp16 shd", "fp16", "shd", 1, 4, 300, 417, 64, sm_scale=0.5, seed=9)
+    full_bwd_parity(w)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.0])
+def test_bwd_scales(scale):
+    w = synth.custom("bwd bf16 scale", "bf16", "bhsd", 1, 2, 96, 130, 64, causal=True, seed=11)
+    full_bwd_parity(w, sm_scale=scale, tag=f" scale {scale}")
+
+
+def test_bwd_keys_no_query_sees():
+    # causal with seq_k > seq_q: keys >= seq_q are visible to nobody -> zero dk, dv
+    w = synth.custom("bwd unseen keys", "bf16", "bhsd", 1, 2, 100, 333, 64, causal=True, seed=12)
+    grads, _ = full_bwd_parity(w)
+    assert np.all(grads["dk"][:, :, 100:] == 0) and np.all(grads["dv"][:, :, 100:] == 0)
+
+
+def test_bwd_empty_queries_zero_key_grads():
+    import torch
+    import tiled_attention_04_amd as fa
+    k = torch.randn(1, 2, 77, 64, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn_like(k)
+    q = torch.empty(1, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    o = torch.empty_like(q)
+    do = torch.empty_like(q)
+    lse = torch.empty(1, 2, 0, device="cuda", dtype=torch.float32)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    fa.backward(q, k, v, o, do, lse, causal=False, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0).item() and torch.all(dv == 0).item()
+
+
+def test_bwd_deterministic():
+    w = synth.custom("bwd det", "bf16", "bhsd", 1, 2, 300, 300, 128, causal=True, seed=13)
+    _, g1, _, _ = run_bwd(w)
+    _, g2, _, _ = run_bwd(w)
+    for key in g1:
+        assert np.array_equal(g1[key], g2[key]), key
+
+
+def test_bwd_c5_shape_sampled():
+    """bf16 [1,16,32768,128] causal: dQ of sampled query rows and dK/dV of
+    sampled late keys against the oracle, and over every key the identities
+    sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i (which hold at any size).
+    The late keys are the x8-scaled ones among the last 1024 positions of two
+    heads (they draw real attention mass, so their gradients are not tiny),
+    compared relative to their own magnitude."""
+    w = synth.WORKLOADS["c5"]
+    say(f"[gpu] bwd sampled {w.name}")
+    inp = synth.make_inputs(w)
+    host, grads, causal, scale = run_bwd(w, inputs=inp)
+    rng = np.random.default_rng(5)
+    B, H, S, D = host["q"].shape
+    rows = np.unique(np.concatenate([rng.choice(B * H * S, 48, replace=False),
+                                     [0, S - 1, 5 * S + 4095, 15 * S + S - 1]]))
+    dq_ref = oracle.backward_dq_rows(host["q"], host["k"], host["v"], host["do"], scale, causal,
+                                     rows)
+    check("c5 dq rows", grads["dq"].reshape(-1, D)[rows], dq_ref)
+    late = []
+    for h in (3, 11):
+        idx = inp.stressed_rows[(0, h)]
+        late.append(h * S + idx[idx >= S - 1024])
+    keys = np.unique(np.concatenate(late))
+    assert keys.size >= 8, keys
+    dk_ref, dv_ref = oracle.backward_dkv_rows(host["q"], host["k"], host["v"], host["do"], scale,
+                                              causal, keys)
+    check("c5 dk keys", grads["dk"].reshape(-1, D)[keys], dk_ref, floor=0.0)
+    check("c5 dv keys", grads["dv"].reshape(-1, D)[keys], dv_ref, floor=0.0)
+    # identities over all keys, per (head, dim)
+    dk_sum = grads["dk"].sum(axis=2)
+    dk_rms = np.sqrt((grads["dk"] ** 2).sum(axis=2))
+    say(f"c5 sum_j dK_j: max |sum| / ||dK|| = {np.max(np.abs(dk_sum) / dk_rms):.3e}")
+    assert np.all(np.abs(dk_sum) <= 0.05 * dk_rms + 1e-3)
+    dv_sum = grads["dv"].sum(axis=2)
+    do_sum = host["do"].sum(axis=2)
+    rel = np.abs(dv_sum - do_sum) / np.sqrt((host["do"] ** 2).sum(axis=2))
+    say(f"c5 sum_j dV_j - sum_i dO_i: max rel {rel.max():.3e}")
+    assert rel.max() <= 0.05

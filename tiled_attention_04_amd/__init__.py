@@ -1,13 +1,13 @@
-"""MI355X (gfx950) fused attention forward: thin ctypes binding of libfa_mi355x.so.
+"""MI355X (gfx950) fused attention: thin ctypes binding of libfa_mi355x.so.
 
-The binding only marshals arguments: every step of the attention forward runs
-in the library's HIP kernels.  PyTorch supplies device memory and the stream.
-There is no CPU fallback -- calling into the binding without the built
-library raises.
+The binding only marshals arguments: every step of the attention forward and
+backward runs in the library's HIP kernels.  PyTorch supplies device memory
+and the stream.  There is no CPU fallback -- calling into the binding without
+the built library raises.
 
-``fa_fwd`` mirrors the C entry point of the same name (raw pointers, sizes and
-per-tensor element strides); ``forward`` is the tensor-level convenience
-wrapper.
+``fa_fwd`` and ``fa_bwd`` mirror the C entry points of the same names (raw
+pointers, sizes and per-tensor element strides); ``forward`` and ``backward``
+are the tensor-level convenience wrappers.
 """
 import ctypes
 import math
@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
 FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_LAYOUT", 6: "FA_ERR_HIP", 7: "FA_ERR_SCALE"}
-EXPORTS = ("fa_fwd", "fa_status_string", "fa_last_error", "fa_version")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_status_string", "fa_last_error", "fa_version")
 
 
 class FaStrides(ctypes.Structure):
@@ -49,6 +49,9 @@ def lib():
         L.fa_fwd.restype = ctypes.c_int
         L.fa_fwd.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [FaStrides] * 4 +
                              [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+        L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [FaStrides] * 8 +
+                             [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_status_string.argtypes = [ctypes.c_int]
         L.fa_last_error.restype = ctypes.c_char_p
@@ -65,6 +68,15 @@ def fa_fwd(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_
     st = [s if isinstance(s, FaStrides) else FaStrides(*s) for s in (q_st, k_st, v_st, o_st)]
     return lib().fa_fwd(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, *st,
                         float(sm_scale), int(causal), int(dtype), stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, batch, heads, seq_q, seq_k, head_dim,
+           q_st, k_st, v_st, o_st, do_st, dq_st, dk_st, dv_st, sm_scale, causal, dtype, stream):
+    """Direct call of the C entry point; returns the integer status."""
+    st = [s if isinstance(s, FaStrides) else FaStrides(*s)
+          for s in (q_st, k_st, v_st, o_st, do_st, dq_st, dk_st, dv_st)]
+    return lib().fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, batch, heads, seq_q, seq_k,
+                        head_dim, *st, float(sm_scale), int(causal), int(dtype), stream)
 
 
 def last_error():
@@ -130,3 +142,47 @@ def forward(q, k, v, causal=False, sm_scale=None, layout="bhsd", out=None, lse=N
     if rc != 0:
         raise FaError(rc, last_error())
     return (out, lse) if return_lse else out
+
+
+def backward(q, k, v, o, dout, lse, causal=False, sm_scale=None, layout="bhsd",
+             dq=None, dk=None, dv=None, delta=None):
+    """Gradients of ``forward`` on the current HIP stream.
+
+    o and lse are the forward's outputs for (q, k, v); dout is the gradient
+    of the loss with respect to o (same shape as q).  Returns (dq, dk, dv),
+    each like its input; ``delta`` (fp32 [B, H, Sq], allocated when None)
+    receives rowsum(dout * o).
+    """
+    import torch
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be device tensors")
+    (B, H, Sq, D), q_st = _dims(q, layout)
+    (Bk, Hk, Sk, Dk), k_st = _dims(k, layout)
+    (_, _, Sv, _), v_st = _dims(v, layout)
+    (_, _, So, _), o_st = _dims(o, layout)
+    (_, _, Sd, _), do_st = _dims(dout, layout)
+    if (Bk, Hk, Dk) != (B, H, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, o, dout shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise TypeError("q, k, v, o and dout must share a dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, Sq] tensor")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    (_, _, _, _), dq_st = _dims(dq, layout)
+    (_, _, _, _), dk_st = _dims(dk, layout)
+    (_, _, _, _), dv_st = _dims(dv, layout)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                B, H, Sq, Sk, D, q_st, k_st, v_st, o_st, do_st, dq_st, dk_st, dv_st,
+                sm_scale, causal, _dtype_code(q), stream)
+    if rc != 0:
+        raise FaError(rc, last_error())
+    return dq, dk, dv

@@ -10,6 +10,7 @@
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernels.hpp"
+#include "fa_bwd_kernels.hpp"
 
 namespace {
 
@@ -118,6 +119,58 @@ fa_status_t launch_f32(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   return fail(FA_ERR_HEAD_DIM, "head_dim %lld unsupported", (long long)head_dim);
 }
 
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq(fa::BwdArgs a) {
+  fa::fa_bwd_dq_body<T, D, 4>(a);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkv(fa::BwdArgs a) {
+  fa::fa_bwd_dkv_body<T, D, 8>(a);
+}
+
+template <typename Kernel>
+fa_status_t launch_bwd(Kernel kernel, int64_t grid, int threads, const fa::BwdArgs& args,
+                       void* stream) {
+  if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
+  fa::BwdArgs a = args;
+  void* params[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)grid),
+                                 dim3((unsigned)threads), params, 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+// D (delta), then dQ (query blocks of 128, heaviest causal blocks first), then
+// dK/dV (key blocks of 256), all on `stream`.
+template <typename T, int DP>
+fa_status_t launch_bwd_dp(fa::BwdArgs a, void* stream) {
+  fa_status_t s;
+  const int64_t rows = (int64_t)a.n_bh * a.seq_q;
+  if (rows > 0) {
+    if ((s = launch_bwd(fa::fa_bwd_delta<T>, (rows + 31) / 32, 256, a, stream)) != FA_OK) return s;
+    a.n_tiles = (int32_t)((a.seq_q + 127) / 128);
+    if ((s = launch_bwd(fa_bwd_dq<T, DP>, (int64_t)a.n_bh * a.n_tiles, 256, a, stream)) != FA_OK)
+      return s;
+  }
+  a.n_tiles = (int32_t)((a.seq_k + 255) / 256);
+  return launch_bwd(fa_bwd_dkv<T, DP>, (int64_t)a.n_bh * a.n_tiles, 512, a, stream);
+}
+
+template <typename T>
+fa_status_t launch_bwd_16bit(const fa::BwdArgs& a, int64_t head_dim, void* stream) {
+  if (head_dim <= 32) return launch_bwd_dp<T, 32>(a, stream);
+  if (head_dim <= 64) return launch_bwd_dp<T, 64>(a, stream);
+  if (head_dim <= 80) return launch_bwd_dp<T, 80>(a, stream);
+  if (head_dim <= 96) return launch_bwd_dp<T, 96>(a, stream);
+  return launch_bwd_dp<T, 128>(a, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +229,66 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   }
 }
 
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* dq, void* dk, void* dv,
+                   int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                   fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
+                   fa_strides_t do_st, fa_strides_t dq_st, fa_strides_t dk_st, fa_strides_t dv_st,
+                   float sm_scale, int causal, fa_dtype_t dtype, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || heads < 0 || seq_q < 0)
+    return fail(FA_ERR_SHAPE, "batch, heads and seq_q must be >= 0");
+  if (seq_k < 1) return fail(FA_ERR_SHAPE, "seq_k must be >= 1 (softmax over no keys)");
+  if (seq_q > kInt32Max - 256 || seq_k > kInt32Max - 256 || batch > kInt32Max || heads > kInt32Max ||
+      batch * heads > kInt32Max || batch * heads * seq_q > INT64_MAX / 2)
+    return fail(FA_ERR_SHAPE, "a size exceeds the 32-bit index range");
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (dtype == FA_DTYPE_F32) return fail(FA_ERR_DTYPE, "the backward supports bf16 and fp16 only");
+  if (head_dim < 1 || head_dim > 128 || head_dim % 8 != 0)
+    return fail(FA_ERR_HEAD_DIM, "backward: head_dim %lld must be in 1..128 and a multiple of 8",
+                (long long)head_dim);
+  fa_status_t s;
+  const fa_strides_t* sts[8] = {&q_st, &k_st, &v_st, &o_st, &do_st, &dq_st, &dk_st, &dv_st};
+  const char* names[8] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
+  for (int i = 0; i < 8; ++i)
+    if ((s = check_strides(names[i], *sts[i], 8)) != FA_OK) return s;
+  if (!std::isfinite(sm_scale)) return fail(FA_ERR_SCALE, "sm_scale must be finite");
+  if (batch == 0 || heads == 0) return FA_OK;  // nothing to read or write
+  if (!k || !v || !dk || !dv) return fail(FA_ERR_NULL, "k, v, dk and dv must be non-NULL");
+  if (seq_q > 0 && (!q || !o || !dout || !lse || !delta || !dq))
+    return fail(FA_ERR_NULL, "q, o, dout, lse, delta and dq must be non-NULL");
+  const void* p16[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (int i = 0; i < 8; ++i)
+    if (p16[i] && !aligned(p16[i], 16)) return fail(FA_ERR_LAYOUT, "%s must be 16-byte aligned", names[i]);
+  if ((lse && !aligned(lse, 4)) || (delta && !aligned(delta, 4)))
+    return fail(FA_ERR_LAYOUT, "lse and delta must be 4-byte aligned");
+
+  fa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.q_sb = q_st.batch; a.q_sh = q_st.head; a.q_ss = q_st.seq;
+  a.k_sb = k_st.batch; a.k_sh = k_st.head; a.k_ss = k_st.seq;
+  a.v_sb = v_st.batch; a.v_sh = v_st.head; a.v_ss = v_st.seq;
+  a.o_sb = o_st.batch; a.o_sh = o_st.head; a.o_ss = o_st.seq;
+  a.do_sb = do_st.batch; a.do_sh = do_st.head; a.do_ss = do_st.seq;
+  a.dq_sb = dq_st.batch; a.dq_sh = dq_st.head; a.dq_ss = dq_st.seq;
+  a.dk_sb = dk_st.batch; a.dk_sh = dk_st.head; a.dk_ss = dk_st.seq;
+  a.dv_sb = dv_st.batch; a.dv_sh = dv_st.head; a.dv_ss = dv_st.seq;
+  a.heads = (int32_t)heads;
+  a.seq_q = (int32_t)seq_q;
+  a.seq_k = (int32_t)seq_k;
+  a.head_dim = (int32_t)head_dim;
+  a.n_bh = (int32_t)(batch * heads);
+  a.scale = sm_scale;
+  a.c = std::fmax(std::fabs(sm_scale) * fa::kLog2e, 1e-30f);
+  a.neg_scale = sm_scale < 0.f ? 1 : 0;
+  a.causal = causal ? 1 : 0;
+  a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
+  if (dtype == FA_DTYPE_BF16) return launch_bwd_16bit<__bf16>(a, head_dim, stream);
+  return launch_bwd_16bit<_Float16>(a, head_dim, stream);
+}
+
 const char* fa_status_string(fa_status_t s) {
   switch (s) {
     case FA_OK: return "FA_OK";
@@ -192,6 +305,6 @@ const char* fa_status_string(fa_status_t s) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 }  // extern "C"

@@ -1,0 +1,585 @@
+// fa_bwd_kernels.hpp -- gfx950 (MI355X) kernels of the attention backward.
+//
+// Method: the recomputation form of the FlashAttention-2 backward in
+// "[CS336] Assignment 2: Systems", section "FlashAttention V2": with the
+// forward's logsumexp L and D = rowsum(dO o O),
+//     P = exp(S - L),  dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+//     dQ = scale dS K,  dK = scale dS^T Q,
+// split, as that page's "Backward Pass" section does, into a phase that
+// fixes a query block and walks the keys (dQ) and a phase that fixes a key
+// block and walks the queries (dK, dV), each recomputing P.
+//
+// MI355X design (not taken from the pages):
+//  * three launches: fa_bwd_delta (D, one 8-lane group per row), the dQ
+//    kernel and the dK/dV kernel; every launch writes disjoint outputs, so
+//    there are no atomics and the result is deterministic;
+//  * dQ kernel: the forward's structure.  S^T = K Q^T and dP^T = V dO^T with
+//    v_mfma_f32_32x32x16_{bf16,f16} (K, V from LDS as A operands, the wave's
+//    Q and dO fragments resident in registers as B operands), so lane l owns
+//    query l % 32 and L, D are one register each; dS^T is rounded to the
+//    input type and used straight from registers as the B operand of
+//    dQ^T += K^T dS^T, whose K^T fragments come from LDS with transposing
+//    reads (ds_read_b64_tr_b16);
+//  * dK/dV kernel: 8 waves x 32 keys, each wave's K and V fragments
+//    resident in registers; Q and dO tiles of 32 queries stream through LDS.
+//    S^T and dP^T as above; P and dS (input type) go through a 4 KiB
+//    per-wave LDS scratch in [query][key] order and come back through
+//    transposing reads as key-major operands of dV^T += dO^T P and
+//    dK^T += Q^T dS, whose dO^T / Q^T fragments are transposing reads of the
+//    streamed tiles;
+//  * tiles read both row-wise (ds_read_b128) and transposed use a row stride
+//    s with s/16 odd and s, 2s, 3s (mod 256) at least 32 bytes from a
+//    multiple of 256, so neither access pattern has bank conflicts;
+//  * K/V (dQ kernel) and Q/dO (dK/dV kernel) tiles are double-buffered with
+//    direct-to-LDS buffer loads; rows past the sequence end and dims past
+//    head_dim arrive as zeros, and P is forced to 0 wherever a key is masked
+//    (causal, key tail) or a query does not exist.
+#pragma once
+#include "fa_fwd_kernels.hpp"
+
+namespace fa {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [n_bh, seq_q], natural log
+  float* delta;      // [n_bh, seq_q], written by fa_bwd_delta
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_sh, q_ss;  // element strides: batch, head, seq (dim stride is 1)
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t do_sb, do_sh, do_ss;
+  int64_t dq_sb, dq_sh, dq_ss;
+  int64_t dk_sb, dk_sh, dk_ss;
+  int64_t dv_sb, dv_sh, dv_ss;
+  int32_t heads, seq_q, seq_k, head_dim;
+  int32_t n_tiles;    // workgroups per (batch, head) of the launch
+  int32_t n_bh;       // batch * heads
+  float scale;        // sm_scale (signed)
+  float c;            // |sm_scale| * log2(e), at least 1e-30
+  int32_t neg_scale;  // sm_scale < 0: one score operand is negated in registers
+  int32_t causal;
+  int32_t xcd_remap;  // n_bh % 8 == 0: keep one (batch, head) on one XCD
+};
+
+// Workgroup id -> (batch*head, tile), grouping the tiles of one (batch, head)
+// on one XCD; `reverse` hands out the last tiles first.
+__device__ inline void map_bwd_workgroup(const BwdArgs& a, int wg, bool reverse, int& bh,
+                                         int& tile) {
+  int rank;
+  if (a.xcd_remap) {
+    const int per = a.n_bh >> 3;
+    const int xcd = wg & 7, slot = wg >> 3;
+    bh = xcd * per + slot % per;
+    rank = slot / per;
+  } else {
+    bh = wg % a.n_bh;
+    rank = wg / a.n_bh;
+  }
+  tile = reverse ? a.n_tiles - 1 - rank : rank;
+}
+
+// Smallest row stride (bytes, multiple of 16, >= min_bytes) that is free of
+// bank conflicts both for 16 lanes reading 16 consecutive rows at one 16-byte
+// chunk and for 16 lanes reading 4 consecutive rows x 32 bytes.
+constexpr int dual_stride(int min_bytes) {
+  int st = (min_bytes + 15) / 16 * 16;
+  for (;; st += 16) {
+    const int s = st % 256;
+    bool ok = ((s / 16) % 2) == 1;
+    for (int m = 1; m <= 3; ++m) {
+      const int r = (m * s) % 256;
+      ok = ok && r >= 32 && r <= 224;
+    }
+    if (ok) return st;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_t dO_it O_it  (fp32), 8 lanes per row, 16 dims per lane.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void fa_bwd_delta(BwdArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 32 + (tid >> 3);
+  const int sub = tid & 7;
+  const int64_t rows = (int64_t)a.n_bh * a.seq_q;
+  float part = 0.f;
+  if (row < rows) {
+    const int bh = (int)(row / a.seq_q), i = (int)(row - (int64_t)bh * a.seq_q);
+    const int b = bh / a.heads, h = bh - b * a.heads;
+    const T* orow = (const T*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)i * a.o_ss;
+    const T* drow =
+        (const T*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)i * a.do_ss;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int d0 = sub * 16 + half * 8;
+      if (d0 < a.head_dim) {
+        typedef T t8 __attribute__((ext_vector_type(8)));
+        const t8 ov = *(const t8*)(orow + d0);
+        const t8 dv = *(const t8*)(drow + d0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)dv[e], (float)ov[e], part);
+      }
+    }
+  }
+  // sum over the 8 lanes of the row
+  part += __shfl_xor(part, 1, 8);
+  part += __shfl_xor(part, 2, 8);
+  part += __shfl_xor(part, 4, 8);
+  if (row < rows && sub == 0) a.delta[row] = part;
+}
+
+// Per-lane byte offsets for direct-to-LDS loads of a tile of `rows` rows of
+// `slots` 16-byte LDS slots each (slot s of the tile is filled by lane s % 64
+// of instruction s / 64); slots past the tile or past head_dim read nothing.
+__device__ inline uint32_t tile_slot_offset(int slot, int rows, int slots, int64_t seq_stride,
+                                            int head_dim) {
+  const int row = slot / slots, ch = slot - (slot / slots) * slots;
+  return (row < rows && ch * 8 < head_dim) ? (uint32_t)(row * (int32_t)seq_stride * 2 + ch * 16)
+                                           : kOutOfRange;
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel: one workgroup per (batch*head, block of 32*NW queries).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW>
+struct BwdQTile {
+  static constexpr int BM = 32 * NW;             // query rows per workgroup
+  static constexpr int BN = 64;                  // keys per K/V tile
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = (D + 31) / 32;
+  static constexpr int KR = dual_stride(D * 2);  // K rows: b128 + transposed
+  static constexpr int VR = D * 2 + 16;          // V rows: b128 only (16 mod 256)
+  static constexpr int KSLOTS = KR / 16, VSLOTS = VR / 16;
+  static constexpr int KINSTR = BN * KSLOTS / 64, VINSTR = BN * VSLOTS / 64;
+  static constexpr int KPER = (KINSTR + NW - 1) / NW, VPER = (VINSTR + NW - 1) / NW;
+  static constexpr int KBYTES = BN * KR, VBYTES = BN * VR;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static_assert(D % 16 == 0 && D <= 128, "head_dim padding");
+  static_assert(KR >= DBLK * 64, "transposed reads of the K tile stay inside a row");
+};
+
+template <typename T, int D, int NW>
+__device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
+  using G = BwdQTile<T, D, NW>;
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
+  constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK, KR = G::KR, VR = G::VR;
+
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
+  FA_LDS char* lds = (FA_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  int bh, qt;
+  map_bwd_workgroup(a, blockIdx.x, a.causal != 0, bh, qt);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const T* qg = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const T* dog = (const T*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh;
+  const T* kg = (const T*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const T* vg = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  T* dqg = (T*)a.dq + (int64_t)b * a.dq_sb + (int64_t)h * a.dq_sh;
+
+  const int q0 = qt * G::BM;
+  const int qw = q0 + wave * 32;
+  const int my_q = qw + l32;
+  const int wave_rows = max(0, min(32, a.seq_q - qw));
+  const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + G::BM)) : a.seq_k;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  // resident fragments (B operands): lane = (query l32, dims 8*hi..+7 of each k-step)
+  frag qf[KSTEPS], dof[KSTEPS];
+  {
+    const int32_t nq = wave_rows > 0 ? (wave_rows - 1) * (int32_t)a.q_ss * 2 + a.head_dim * 2 : 0;
+    const int32_t nd = wave_rows > 0 ? (wave_rows - 1) * (int32_t)a.do_ss * 2 + a.head_dim * 2 : 0;
+    const auto rq = make_rsrc(qg + (int64_t)(wave_rows > 0 ? qw : 0) * a.q_ss, nq);
+    const auto rd = make_rsrc(dog + (int64_t)(wave_rows > 0 ? qw : 0) * a.do_ss, nd);
+    const uint32_t sign = a.neg_scale ? 0x80008000u : 0u;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      const int col = st * 16 + hi * 8;
+      const bool in = col < a.head_dim;
+      u32x4_t rawq = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, in ? (uint32_t)(l32 * (int32_t)a.q_ss * 2 + col * 2) : kOutOfRange, 0, 0);
+      const u32x4_t rawd = __builtin_amdgcn_raw_buffer_load_b128(
+          rd, in ? (uint32_t)(l32 * (int32_t)a.do_ss * 2 + col * 2) : kOutOfRange, 0, 0);
+      rawq ^= (u32x4_t){sign, sign, sign, sign};
+      qf[st] = __builtin_bit_cast(frag, rawq);
+      dof[st] = __builtin_bit_cast(frag, rawd);
+    }
+  }
+  const bool q_ok = my_q < a.seq_q;
+  const float L2 = q_ok ? a.lse[(int64_t)bh * a.seq_q + my_q] * kLog2e : 0.f;
+  const float Dl = q_ok ? a.delta[(int64_t)bh * a.seq_q + my_q] : 0.f;
+  const float c = a.c;
+
+  // direct-to-LDS tile loads, all NW waves
+  uint32_t koff[G::KPER], voff[G::VPER];
+#pragma unroll
+  for (int n = 0; n < G::KPER; ++n)
+    koff[n] = tile_slot_offset((wave + NW * n) * 64 + lane, BN, G::KSLOTS, a.k_ss, a.head_dim);
+#pragma unroll
+  for (int n = 0; n < G::VPER; ++n)
+    voff[n] = tile_slot_offset((wave + NW * n) * 64 + lane, BN, G::VSLOTS, a.v_ss, a.head_dim);
+  auto issue = [&](int j, int stage) {
+    const int key0 = j * BN;
+    const int rows = min(BN, a.seq_k - key0);
+    const auto rk = make_rsrc(kg + (int64_t)key0 * a.k_ss, (rows - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2);
+    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
+    FA_LDS char* kb = lds + stage * G::STAGE;
+    FA_LDS char* vb = kb + G::KBYTES;
+#pragma unroll
+    for (int n = 0; n < G::KPER; ++n)
+      if (wave + NW * n < G::KINSTR)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(kb + (wave + NW * n) * 1024), 16,
+                                                 koff[n], 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < G::VPER; ++n)
+      if (wave + NW * n < G::VINSTR)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(vb + (wave + NW * n) * 1024), 16,
+                                                 voff[n], 0, 0, 0);
+  };
+
+  f32x16_t acc[DBLK];  // dQ^T: rows = dims of block db, column = query l32
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) acc[db] = (f32x16_t){};
+
+  const int k_lane = l32 * KR + hi * 16;  // b128 row reads of K
+  const int v_lane = l32 * VR + hi * 16;  // b128 row reads of V
+  const int s16 = lane & 15;
+  const int t_lane = (4 * hi + (s16 >> 2)) * KR + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+
+  if (n_tiles > 0) {
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < n_tiles) issue(t + 1, stage ^ 1);
+    FA_LDS char* kb = lds + stage * G::STAGE;
+    FA_LDS char* vb = kb + G::KBYTES;
+
+    // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks of the tile
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s[kb2] = (f32x16_t){};
+      dp[kb2] = (f32x16_t){};
+    }
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const frag kf = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(kb + k_lane + kb2 * 32 * KR + st * 32));
+        const frag vf = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(vb + v_lane + kb2 * 32 * VR + st * 32));
+        s[kb2] = M::mma(kf, qf[st], s[kb2]);
+        dp[kb2] = M::mma(vf, dof[st], dp[kb2]);
+      }
+
+    // P = exp2(s c - L2) (0 where masked), dS = P (dP - D), rounded pairwise
+    const int key0 = t * BN;
+    const bool need_mask = (key0 + BN > a.seq_k) || (a.causal && key0 + BN - 1 > qw);
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -L2));
+        float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -L2));
+        if (need_mask) {
+          const int kk = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          p0 = (kk < a.seq_k && (!a.causal || kk <= my_q)) ? p0 : 0.f;
+          p1 = (kk + 1 < a.seq_k && (!a.causal || kk + 1 <= my_q)) ? p1 : 0.f;
+        }
+        pk[kb2][r >> 1] = M::pack2(p0 * (dp[kb2][r] - Dl), p1 * (dp[kb2][r + 1] - Dl));
+      }
+
+    // dQ^T += K^T dS^T: four 16-key steps per 32-dim block
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4_t sraw = {pk[u >> 1][4 * (u & 1) + 0], pk[u >> 1][4 * (u & 1) + 1],
+                            pk[u >> 1][4 * (u & 1) + 2], pk[u >> 1][4 * (u & 1) + 3]};
+      const frag sf = __builtin_bit_cast(frag, sraw);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        FA_LDS char* p0 = kb + t_lane + (16 * u) * KR + db * 64;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p0);
+        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + 8 * KR));
+        const u32x4_t kraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                              __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
+        acc[db] = M::mma(__builtin_bit_cast(frag, kraw), sf, acc[db]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
+    __syncthreads();                // ... and everyone's; stage t is free
+  }
+
+  // dQ = scale * (K^T dS^T)^T, rounded to the input type
+  if (wave_rows == 0) return;
+  const int32_t onrec = (wave_rows - 1) * (int32_t)a.dq_ss * 2 + a.head_dim * 2;
+  const auto ro = make_rsrc(dqg + (int64_t)qw * a.dq_ss, onrec);
+  const uint32_t orow = (uint32_t)(l32 * (int32_t)a.dq_ss * 2);
+  const float sc = a.scale;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + 8 * g + 4 * hi;
+      const uint32_t off = (d0 < a.head_dim && l32 < wave_rows) ? orow + d0 * 2 : kOutOfRange;
+      const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * sc, acc[db][4 * g + 1] * sc),
+                         M::pack2(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel: one workgroup per (batch*head, block of 32*NW keys).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW>
+struct BwdKVTile {
+  static constexpr int BK = 32 * NW;             // keys per workgroup
+  static constexpr int BQ = 32;                  // queries per streamed tile
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = (D + 31) / 32;
+  static constexpr int QR = dual_stride(D * 2);  // Q / dO rows: b128 + transposed
+  static constexpr int QSLOTS = QR / 16;
+  static constexpr int QINSTR = (BQ * QSLOTS + 63) / 64;  // wave-wide loads per tile
+  static constexpr int QPER = (QINSTR + NW - 1) / NW;
+  static constexpr int TBYTES = QINSTR * 1024;   // one tile, rounded to whole loads
+  static constexpr int STAGE = 2 * TBYTES;       // Q tile + dO tile
+  static constexpr int PROW = 64;                // scratch row: 32 keys x 2 bytes
+  static constexpr int SCRATCH = 2 * BQ * PROW;  // P and dS of one wave
+  static constexpr int LDS_BYTES = 2 * STAGE + NW * SCRATCH;
+  static_assert(D % 16 == 0 && D <= 128, "head_dim padding");
+  static_assert(QR >= DBLK * 64, "transposed reads stay inside a row");
+};
+
+// Byte offset of element (query row, key col) in a wave's P / dS scratch:
+// 64-byte rows, 16-byte chunks XOR-swizzled by (row / 4) % 4 so that the
+// row-wise writes of the 32 lanes spread over the banks.
+__device__ inline int scratch_off(int row, int col_bytes) {
+  return row * 64 + ((col_bytes & ~48) | (((col_bytes >> 4) ^ (row >> 2)) & 3) << 4);
+}
+
+template <typename T, int D, int NW>
+__device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
+  using G = BwdKVTile<T, D, NW>;
+  using M = Mfma<T>;
+  typedef typename M::frag frag;
+  constexpr int BQ = G::BQ, KSTEPS = G::KSTEPS, DBLK = G::DBLK, QR = G::QR;
+
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
+  FA_LDS char* lds = (FA_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  int bh, kt;
+  map_bwd_workgroup(a, blockIdx.x, false, bh, kt);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const T* qg = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const T* dog = (const T*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh;
+  const T* kg = (const T*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const T* vg = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  T* dkg = (T*)a.dk + (int64_t)b * a.dk_sb + (int64_t)h * a.dk_sh;
+  T* dvg = (T*)a.dv + (int64_t)b * a.dv_sb + (int64_t)h * a.dv_sh;
+  const float* lseg = a.lse + (int64_t)bh * a.seq_q;
+  const float* delg = a.delta + (int64_t)bh * a.seq_q;
+
+  const int k0 = kt * G::BK;
+  const int kw = k0 + wave * 32;        // first key of this wave
+  const int wave_keys = max(0, min(32, a.seq_k - kw));
+  // query tiles that see any key of the workgroup (causal: queries >= k0)
+  const int qt0 = a.causal ? min(k0, a.seq_q) / BQ : 0;
+  const int qt_end = (a.seq_q + BQ - 1) / BQ;
+
+  // resident A operands: lane = (key l32, dims 8*hi..+7 of each k-step); K negated for scale < 0
+  frag kf[KSTEPS], vf[KSTEPS];
+  {
+    const int32_t nk = wave_keys > 0 ? (wave_keys - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2 : 0;
+    const int32_t nv = wave_keys > 0 ? (wave_keys - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2 : 0;
+    const auto rk = make_rsrc(kg + (int64_t)(wave_keys > 0 ? kw : 0) * a.k_ss, nk);
+    const auto rv = make_rsrc(vg + (int64_t)(wave_keys > 0 ? kw : 0) * a.v_ss, nv);
+    const uint32_t sign = a.neg_scale ? 0x80008000u : 0u;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      const int col = st * 16 + hi * 8;
+      const bool in = col < a.head_dim;
+      u32x4_t rawk = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, in ? (uint32_t)(l32 * (int32_t)a.k_ss * 2 + col * 2) : kOutOfRange, 0, 0);
+      const u32x4_t rawv = __builtin_amdgcn_raw_buffer_load_b128(
+          rv, in ? (uint32_t)(l32 * (int32_t)a.v_ss * 2 + col * 2) : kOutOfRange, 0, 0);
+      rawk ^= (u32x4_t){sign, sign, sign, sign};
+      kf[st] = __builtin_bit_cast(frag, rawk);
+      vf[st] = __builtin_bit_cast(frag, rawv);
+    }
+  }
+  const float c = a.c;
+
+  // direct-to-LDS loads of the Q and dO tiles, all NW waves
+  uint32_t qoff[G::QPER], doff[G::QPER];
+#pragma unroll
+  for (int n = 0; n < G::QPER; ++n) {
+    const int slot = (wave + NW * n) * 64 + lane;
+    qoff[n] = tile_slot_offset(slot, BQ, G::QSLOTS, a.q_ss, a.head_dim);
+    doff[n] = tile_slot_offset(slot, BQ, G::QSLOTS, a.do_ss, a.head_dim);
+  }
+  auto issue = [&](int j, int stage) {
+    const int qa = j * BQ;
+    const int rows = min(BQ, a.seq_q - qa);
+    const auto rq = make_rsrc(qg + (int64_t)qa * a.q_ss, (rows - 1) * (int32_t)a.q_ss * 2 + a.head_dim * 2);
+    const auto rd = make_rsrc(dog + (int64_t)qa * a.do_ss, (rows - 1) * (int32_t)a.do_ss * 2 + a.head_dim * 2);
+    FA_LDS char* qb = lds + stage * G::STAGE;
+    FA_LDS char* db_ = qb + G::TBYTES;
+#pragma unroll
+    for (int n = 0; n < G::QPER; ++n)
+      if (wave + NW * n < G::QINSTR) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (FA_LDS void*)(qb + (wave + NW * n) * 1024), 16,
+                                                 qoff[n], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(db_ + (wave + NW * n) * 1024), 16,
+                                                 doff[n], 0, 0, 0);
+      }
+  };
+
+  // dV^T and dK^T: rows = dims of block db, column = key l32
+  f32x16_t dvacc[DBLK], dkacc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    dvacc[db] = (f32x16_t){};
+    dkacc[db] = (f32x16_t){};
+  }
+
+  FA_LDS char* pscr = lds + 2 * G::STAGE + wave * G::SCRATCH;  // P, then dS at + BQ * PROW
+  const int q_lane = l32 * QR + hi * 16;                          // b128 row reads of Q / dO
+  const int s16 = lane & 15;
+  const int t_row = 4 * hi + (s16 >> 2);                          // transposing reads
+  const int t_col = (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+  const int t_lane = t_row * QR + t_col;
+
+  if (qt0 < qt_end) {
+    issue(qt0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int t = qt0; t < qt_end; ++t) {
+    const int stage = (t - qt0) & 1;
+    if (t + 1 < qt_end) issue(t + 1, stage ^ 1);
+    FA_LDS char* qb = lds + stage * G::STAGE;
+    FA_LDS char* dob = qb + G::TBYTES;
+
+    // S^T = K Q^T, dP^T = V dO^T: rows = this wave's 32 keys, column = query l32
+    f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      const frag qfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + q_lane + st * 32));
+      const frag dfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + q_lane + st * 32));
+      s = M::mma(kf[st], qfr, s);
+      dp = M::mma(vf[st], dfr, dp);
+    }
+
+    const int qa = t * BQ;
+    const int my_q = qa + l32;
+    const bool q_ok = my_q < a.seq_q;
+    const float L2 = q_ok ? lseg[my_q] * kLog2e : 0.f;
+    const float Dl = q_ok ? delg[my_q] : 0.f;
+    const bool need_mask = !q_ok || (qa + BQ > a.seq_q) || (kw + 32 > a.seq_k) ||
+                           (a.causal && kw + 31 > qa);
+    // P and dS in the input type, written to the scratch in [query][key] order
+    uint32_t pp[8], ps[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0 = fast_exp2(__builtin_fmaf(s[r], c, -L2));
+      float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -L2));
+      if (need_mask) {
+        const int kk = kw + 8 * (r >> 2) + 4 * hi + (r & 3);
+        p0 = (q_ok && kk < a.seq_k && (!a.causal || kk <= my_q)) ? p0 : 0.f;
+        p1 = (q_ok && kk + 1 < a.seq_k && (!a.causal || kk + 1 <= my_q)) ? p1 : 0.f;
+      }
+      pp[r >> 1] = M::pack2(p0, p1);
+      ps[r >> 1] = M::pack2(p0 * (dp[r] - Dl), p1 * (dp[r + 1] - Dl));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = scratch_off(l32, (8 * j + 4 * hi) * 2);
+      *(FA_LDS u32x2_t*)(pscr + off) = (u32x2_t){pp[2 * j], pp[2 * j + 1]};
+      *(FA_LDS u32x2_t*)(pscr + BQ * G::PROW + off) = (u32x2_t){ps[2 * j], ps[2 * j + 1]};
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS: two 16-query steps per 32-dim block
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      frag pfr, sfr;
+      {
+        const int r0 = 16 * u + t_row;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS i16x4_t*)(pscr + scratch_off(r0, t_col)));
+        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS i16x4_t*)(pscr + scratch_off(r0 + 8, t_col)));
+        const i16x4_t lo2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS i16x4_t*)(pscr + BQ * G::PROW + scratch_off(r0, t_col)));
+        const i16x4_t up2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FA_LDS i16x4_t*)(pscr + BQ * G::PROW + scratch_off(r0 + 8, t_col)));
+        const u32x4_t praw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                              __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
+        const u32x4_t sraw = {__builtin_bit_cast(u32x2_t, lo2)[0], __builtin_bit_cast(u32x2_t, lo2)[1],
+                              __builtin_bit_cast(u32x2_t, up2)[0], __builtin_bit_cast(u32x2_t, up2)[1]};
+        pfr = __builtin_bit_cast(frag, praw);
+        sfr = __builtin_bit_cast(frag, sraw);
+      }
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        FA_LDS char* d0 = dob + t_lane + (16 * u) * QR + db * 64;
+        FA_LDS char* q0p = qb + t_lane + (16 * u) * QR + db * 64;
+        const i16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)d0);
+        const i16x4_t dup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(d0 + 8 * QR));
+        const i16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)q0p);
+        const i16x4_t qup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(q0p + 8 * QR));
+        const u32x4_t draw = {__builtin_bit_cast(u32x2_t, dlo)[0], __builtin_bit_cast(u32x2_t, dlo)[1],
+                              __builtin_bit_cast(u32x2_t, dup)[0], __builtin_bit_cast(u32x2_t, dup)[1]};
+        const u32x4_t qraw = {__builtin_bit_cast(u32x2_t, qlo)[0], __builtin_bit_cast(u32x2_t, qlo)[1],
+                              __builtin_bit_cast(u32x2_t, qup)[0], __builtin_bit_cast(u32x2_t, qup)[1]};
+        dvacc[db] = M::mma(__builtin_bit_cast(frag, draw), pfr, dvacc[db]);
+        dkacc[db] = M::mma(__builtin_bit_cast(frag, qraw), sfr, dkacc[db]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
+    __syncthreads();                // ... and everyone's; stage t is free
+  }
+
+  // dK = scale * dK^T^T, dV = dV^T^T, rounded to the input type
+  if (wave_keys == 0) return;
+  const auto rdk = make_rsrc(dkg + (int64_t)kw * a.dk_ss, (wave_keys - 1) * (int32_t)a.dk_ss * 2 + a.head_dim * 2);
+  const auto rdv = make_rsrc(dvg + (int64_t)kw * a.dv_ss, (wave_keys - 1) * (int32_t)a.dv_ss * 2 + a.head_dim * 2);
+  const uint32_t krow = (uint32_t)(l32 * (int32_t)a.dk_ss * 2);
+  const uint32_t vrow = (uint32_t)(l32 * (int32_t)a.dv_ss * 2);
+  const float sc = a.scale;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + 8 * g + 4 * hi;
+      const bool ok = d0 < a.head_dim && l32 < wave_keys;
+      const u32x2_t wk = {M::pack2(dkacc[db][4 * g + 0] * sc, dkacc[db][4 * g + 1] * sc),
+                          M::pack2(dkacc[db][4 * g + 2] * sc, dkacc[db][4 * g + 3] * sc)};
+      const u32x2_t wv = {M::pack2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]),
+                          M::pack2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
+      __builtin_amdgcn_raw_buffer_store_b64(wk, rdk, ok ? krow + d0 * 2 : kOutOfRange, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(wv, rdv, ok ? vrow + d0 * 2 : kOutOfRange, 0, 0);
+    }
+}
+
+}  // namespace fa

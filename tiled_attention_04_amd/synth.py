@@ -170,6 +170,22 @@ def make_inputs(w, seq_q=None, seq_k=None):
     return Inputs(w, q, k, v, stressed)
 
 
+def make_dout(w):
+    """The upstream gradient dO of workload ``w`` for the backward: N(0, 1)
+    draws in the shape (and layout) of q, rounded once to the dtype, from its
+    own stream (seed + 7919) so the forward inputs are unchanged."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(w.seed + 7919)
+    return _draw(rng, w.shape("q"), 1.0, w.dtype)
+
+
+def dout_bhsd_f64(w, dout):
+    """dO as float64 in [B, H, S, D] order."""
+    arr = np.transpose(dout, (1, 0, 2))[None] if w.layout == "shd" else dout
+    return widen(arr, w.dtype)
+
+
 def custom(name, dtype, layout, batch, heads, seq_q, seq_k, head_dim, std=1.0, sm_scale=None,
            causal=False, seed=0, stress_frac=0.0, stress_factor=1.0):
     """A Workload for edge-case tests (same recipe, other sizes)."""
