@@ -186,3 +186,38 @@ def test_bwd_c5_shape_sampled():
     rel = np.abs(dv_sum - do_sum) / np.sqrt((host["do"] ** 2).sum(axis=2))
     say(f"c5 sum_j dV_j - sum_i dO_i: max rel {rel.max():.3e}")
     assert rel.max() <= 0.05
+
+
+def test_autograd_function_matches_direct_calls_and_oracle():
+    """loss.backward() through tiled_attention_04_amd.autograd.attention gives
+    exactly the gradients of the direct fa_bwd call, which match the oracle;
+    an expanded (stride-0) upstream gradient is accepted."""
+    import torch
+    import tiled_attention_04_amd as fa
+    from tiled_attention_04_amd.autograd import attention
+    w = synth.custom("autograd bf16", "bf16", "bhsd", 1, 2, 150, 150, 64, causal=True, seed=21)
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    q, k, v = (to_device(x, w.dtype).requires_grad_(True) for x in (inp.q, inp.k, inp.v))
+    do = to_device(dout, w.dtype)
+    o = attention(q, k, v, causal=True)
+    (o * do).sum().backward()
+    with torch.no_grad():
+        o2, lse2 = fa.forward(q, k, v, causal=True)
+        dq, dk, dv = fa.backward(q, k, v, o2, do, lse2, causal=True)
+    torch.cuda.synchronize()
+    for g_auto, g_direct in ((q.grad, dq), (k.grad, dk), (v.grad, dv)):
+        assert torch.equal(g_auto, g_direct)
+    ref = oracle.backward(inp.as_bhsd_f64("q"), inp.as_bhsd_f64("k"), inp.as_bhsd_f64("v"),
+                          synth.dout_bhsd_f64(w, dout), w.sm_scale, True)
+    for name, g, r in (("dq", q.grad, ref[0]), ("dk", k.grad, ref[1]), ("dv", v.grad, ref[2])):
+        check(f"autograd {name}", device_to_f64(g), r)
+    # o.sum() hands back an expanded gradient of ones (all strides 0)
+    for t in (q, k, v):
+        t.grad = None
+    attention(q, k, v, causal=True).sum().backward()
+    torch.cuda.synchronize()
+    ones = np.ones(dout.shape)
+    ref1 = oracle.backward(inp.as_bhsd_f64("q"), inp.as_bhsd_f64("k"), inp.as_bhsd_f64("v"),
+                           ones, w.sm_scale, True)
+    check("autograd ones dv", device_to_f64(v.grad), ref1[2])
