@@ -15,7 +15,10 @@ Prints one JSON line:
              of the same workload on this host
 
 Other modes:
-  --workload c2|c3|c4   time another workload (not the default line)
+  --workload c2|c3|c4   time another workload (not the default line); also
+                        short100 / short10 (few queries against 4096 keys)
+  --splits S            forward through fa_fwd_splitk with S key splits (0: the
+                        library's choice)
   --copy-calib          also run a plain device copy of 1 GiB (for counter
                         calibration under rocprofv3 --pmc)
   --summarize-pmc DIR   reduce rocprofv3 --pmc output under DIR to a summary
@@ -182,11 +185,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5",
+                    choices=["c2", "c3", "c4", "c5", "short100", "short10"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-pmc", default=None)
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
+    ap.add_argument("--splits", type=int, default=1,
+                    help="forward through fa_fwd_splitk with this many key splits "
+                         "(0: the library's choice; 1: plain fa_fwd)")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -207,7 +214,7 @@ def main():
     fa.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS.get(args.workload) or synth.EXTRA_WORKLOADS[args.workload]
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w)
 
@@ -225,6 +232,18 @@ def main():
 
     def step():
         fa.forward(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout, out=o, lse=lse)
+
+    splits = 1
+    if args.splits != 1 and args.which == "fwd":
+        splits = args.splits or fa.fa_fwd_splitk_choose(w.batch, w.heads, w.seq_q, w.seq_k,
+                                                         w.head_dim, w.causal)
+        ws = torch.empty(max(1, fa.fa_fwd_splitk_workspace(w.batch, w.heads, w.seq_q,
+                                                           w.head_dim, splits)),
+                         dtype=torch.uint8, device=dev)
+
+        def step():  # noqa: F811
+            fa.forward_splitk(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout,
+                              num_splits=splits, out=o, lse=lse, workspace=ws)
 
     if args.which == "bwd":
         return bench_bwd(args, w, inp, up, q, k, v, o, lse, layout, stream)
@@ -283,7 +302,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_q": w.seq_q,
+        "config": {"workload": w.name, "key_splits": splits, "batch": w.batch, "heads": w.heads,
+                   "seq_q": w.seq_q,
                    "seq_k": w.seq_k, "head_dim": w.head_dim, "causal": w.causal,
                    "sm_scale": w.sm_scale, "flops_per_step": flops},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -18,6 +18,7 @@
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -39,7 +40,9 @@ typedef enum {
   FA_ERR_HEAD_DIM = 4,  /* head_dim outside 1..256, or not a multiple of 8 (16-bit) / 4 (fp32) */
   FA_ERR_LAYOUT = 5,    /* dim stride != 1, negative stride, or misaligned pointer/stride */
   FA_ERR_HIP = 6,       /* the HIP runtime reported an error when launching */
-  FA_ERR_SCALE = 7      /* sm_scale is NaN or infinite */
+  FA_ERR_SCALE = 7,     /* sm_scale is NaN or infinite */
+  FA_ERR_WORKSPACE = 8  /* fa_fwd_splitk: num_splits outside 0..16, or the workspace is
+                           missing, misaligned or too small */
 } fa_status_t;
 
 /* Strides of one 4-D tensor, in ELEMENTS (not bytes), for the logical
@@ -97,6 +100,49 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
                    fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
                    float sm_scale, int causal, fa_dtype_t dtype, void* stream);
+
+/*
+ * fa_fwd_splitk -- fa_fwd with the keys of every query tile split over
+ * num_splits workgroups, for grids too small to fill the GPU (few query
+ * tiles per head: short queries, few heads).  Each split runs the forward on
+ * its share of the key tiles and writes fp32 partials (O_r normalised by its
+ * own row sum, lse_r); a second launch merges them with
+ *     lse = log sum_r exp(lse_r),   O = sum_r exp(lse_r - lse) O_r,
+ * the combination of two online-softmax states ("[CS336] Assignment 2:
+ * Systems", section "FlashAttention V2": the running max and sum are merged
+ * by rescaling with exp of the max difference; the logsumexp is the state in
+ * one number).  Same arguments, semantics, layouts and ownership as fa_fwd,
+ * plus:
+ *   num_splits       0 = fa_fwd_splitk_choose(...); 1 = no splitting (then
+ *                    identical to fa_fwd and no workspace is used); 2..16
+ *   workspace        caller-owned device memory, 256-byte aligned, of at least
+ *                    fa_fwd_splitk_workspace(batch, heads, seq_q, head_dim,
+ *                    splits) bytes (fp32 partials); contents are overwritten
+ *   workspace_bytes  its size.
+ * Key splitting needs bf16/fp16 (fp32 with num_splits > 1 -> FA_ERR_DTYPE);
+ * num_splits outside 0..16 or a missing/misaligned/short workspace ->
+ * FA_ERR_WORKSPACE (checked after the fa_fwd checks, before any HIP call).
+ * O is rounded once, after the merge.  Two calls that share a workspace on
+ * different streams race.
+ */
+fa_status_t fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                          int64_t head_dim, fa_strides_t q_st, fa_strides_t k_st,
+                          fa_strides_t v_st, fa_strides_t o_st, float sm_scale, int causal,
+                          fa_dtype_t dtype, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Number of key splits fa_fwd_splitk uses for num_splits == 0: about one
+ * workgroup per CU, at least eight 64-key tiles per split, at most 16; 1
+ * when the unsplit grid already has 256 workgroups.  Never fails (1 for empty
+ * or invalid sizes). */
+int fa_fwd_splitk_choose(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                         int64_t head_dim, int causal);
+
+/* Workspace bytes fa_fwd_splitk needs for `num_splits` splits (0 when
+ * num_splits <= 1 or a size is not positive). */
+size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int64_t head_dim,
+                               int num_splits);
 
 /*
  * fa_bwd -- enqueue the gradients of fa_fwd on `stream` and return.

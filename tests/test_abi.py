@@ -115,3 +115,36 @@ def test_bwd_empty_problem_is_ok_without_pointers():
         assert fa.last_error() == ""
     # without queries dk and dv are still written (zeros), so they are required
     assert call_bwd(**nothing, sq=0) == 1
+
+
+def call_splitk(splits=2, ws=P, ws_bytes=1 << 30, dtype=BF16, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=None, batch=1, heads=2, sq=128, sk=128, d=64)
+    args.update(kw)
+    return fa.fa_fwd_splitk(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                            args["batch"], args["heads"], args["sq"], args["sk"], args["d"],
+                            CONTIG, CONTIG, CONTIG, CONTIG, 0.125, 0, dtype, splits, ws, ws_bytes,
+                            None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(splits=-1), 8), (dict(splits=17), 8), (dict(ws=None), 8), (dict(ws=P + 16), 8),
+    (dict(ws_bytes=1000), 8), (dict(splits=2, dtype=F32), 3), (dict(sk=0), 2),
+    (dict(q=None), 1),
+])
+def test_splitk_validation_errors(kwargs, code):
+    rc = call_splitk(**kwargs)
+    assert rc == code, (kwargs, rc, fa.last_error())
+    assert fa.last_error() != ""
+
+
+def test_splitk_sizes_and_choice():
+    assert fa.fa_fwd_splitk_workspace(1, 2, 128, 64, 1) == 0
+    assert fa.fa_fwd_splitk_workspace(1, 2, 128, 64, 3) == 3 * 2 * 128 * 65 * 4
+    assert fa.fa_fwd_splitk_workspace(0, 2, 128, 64, 3) == 0
+    # a large grid needs no splitting; a few query tiles against many keys does
+    assert fa.fa_fwd_splitk_choose(1, 16, 32768, 32768, 128, 1) == 1
+    assert fa.fa_fwd_splitk_choose(1, 16, 1000, 1537, 64, 0) > 1
+    assert 1 <= fa.fa_fwd_splitk_choose(1, 1, 10, 100000, 64, 0) <= 16
+    assert fa.fa_fwd_splitk_choose(0, 1, 10, 10, 64, 0) == 1
+    # an empty problem needs no workspace
+    assert call_splitk(batch=0, ws=None, q=None, k=None, v=None, o=None) == 0

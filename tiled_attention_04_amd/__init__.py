@@ -18,8 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
 
 FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
-          4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_LAYOUT", 6: "FA_ERR_HIP", 7: "FA_ERR_SCALE"}
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_status_string", "fa_last_error", "fa_version")
+          4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_LAYOUT", 6: "FA_ERR_HIP", 7: "FA_ERR_SCALE",
+          8: "FA_ERR_WORKSPACE"}
+EXPORTS = ("fa_fwd", "fa_fwd_splitk", "fa_fwd_splitk_choose", "fa_fwd_splitk_workspace",
+           "fa_bwd", "fa_status_string", "fa_last_error", "fa_version")
 
 
 class FaStrides(ctypes.Structure):
@@ -49,6 +51,14 @@ def lib():
         L.fa_fwd.restype = ctypes.c_int
         L.fa_fwd.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [FaStrides] * 4 +
                              [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+        L.fa_fwd_splitk.restype = ctypes.c_int
+        L.fa_fwd_splitk.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [FaStrides] * 4 +
+                                    [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+        L.fa_fwd_splitk_choose.restype = ctypes.c_int
+        L.fa_fwd_splitk_choose.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
+        L.fa_fwd_splitk_workspace.restype = ctypes.c_size_t
+        L.fa_fwd_splitk_workspace.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [FaStrides] * 8 +
                              [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
@@ -68,6 +78,23 @@ def fa_fwd(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_
     st = [s if isinstance(s, FaStrides) else FaStrides(*s) for s in (q_st, k_st, v_st, o_st)]
     return lib().fa_fwd(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, *st,
                         float(sm_scale), int(causal), int(dtype), stream)
+
+
+def fa_fwd_splitk(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_st, o_st,
+                  sm_scale, causal, dtype, num_splits, workspace, workspace_bytes, stream):
+    """Direct call of the C entry point; returns the integer status."""
+    st = [s if isinstance(s, FaStrides) else FaStrides(*s) for s in (q_st, k_st, v_st, o_st)]
+    return lib().fa_fwd_splitk(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, *st,
+                               float(sm_scale), int(causal), int(dtype), int(num_splits),
+                               workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_splitk_choose(batch, heads, seq_q, seq_k, head_dim, causal):
+    return lib().fa_fwd_splitk_choose(batch, heads, seq_q, seq_k, head_dim, int(causal))
+
+
+def fa_fwd_splitk_workspace(batch, heads, seq_q, head_dim, num_splits):
+    return lib().fa_fwd_splitk_workspace(batch, heads, seq_q, head_dim, int(num_splits))
 
 
 def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, batch, heads, seq_q, seq_k, head_dim,
@@ -142,6 +169,40 @@ def forward(q, k, v, causal=False, sm_scale=None, layout="bhsd", out=None, lse=N
     if rc != 0:
         raise FaError(rc, last_error())
     return (out, lse) if return_lse else out
+
+
+def forward_splitk(q, k, v, causal=False, sm_scale=None, layout="bhsd", num_splits=0,
+                   out=None, lse=None, workspace=None):
+    """``forward`` with the keys split over ``num_splits`` workgroups per query
+    tile (0: the library's choice) and merged by logsumexp.  ``workspace`` is a
+    device tensor of at least fa_fwd_splitk_workspace(...) bytes (allocated
+    when None).  Returns (o, lse)."""
+    import torch
+    (B, H, Sq, D), q_st = _dims(q, layout)
+    (Bk, Hk, Sk, Dk), k_st = _dims(k, layout)
+    (Bv, Hv, Sv, Dv), v_st = _dims(v, layout)
+    if (Bk, Hk, Dk) != (B, H, D) or (Bv, Hv, Sv, Dv) != (B, H, Sk, D):
+        raise ValueError("q, k, v shapes disagree")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if num_splits == 0:
+        num_splits = fa_fwd_splitk_choose(B, H, Sq, Sk, D, causal)
+    out = torch.empty_like(q) if out is None else out
+    (_, _, _, _), o_st = _dims(out, layout)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    need = fa_fwd_splitk_workspace(B, H, Sq, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd_splitk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, H, Sq, Sk, D, q_st, k_st, v_st, o_st, sm_scale, causal, _dtype_code(q),
+                       num_splits, ws_ptr, ws_bytes, stream)
+    if rc != 0:
+        raise FaError(rc, last_error())
+    return out, lse
 
 
 def backward(q, k, v, o, dout, lse, causal=False, sm_scale=None, layout="bhsd",

@@ -77,7 +77,7 @@ template <typename T, int NW>
 fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   constexpr int OCC = FA_OCC16;
   a.n_qtiles = (int32_t)((a.seq_q + 32 * NW - 1) / (32 * NW));
-  const int64_t grid = (int64_t)a.n_bh * a.n_qtiles;
+  const int64_t grid = (int64_t)a.n_bh * a.n_qtiles * a.n_splits;
   if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
   a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
 #define FA_CASE(DP)                                                            \
@@ -89,22 +89,63 @@ fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   if (head_dim <= DP) return launch(fa_fwd_16bit<T, DP, 4, 1>, grid4, 256, a4, stream);
   fa::FwdArgs a4 = a;
   a4.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
-  const int64_t grid4 = (int64_t)a.n_bh * a4.n_qtiles;
+  const int64_t grid4 = (int64_t)a.n_bh * a4.n_qtiles * a.n_splits;
   if (grid4 > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid4);
   FA_CASE(160) FA_CASE(192) FA_CASE(256)
 #undef FA_CASE
   return fail(FA_ERR_HEAD_DIM, "head_dim %lld unsupported", (long long)head_dim);
 }
 
+// Waves per workgroup of the 16-bit forward (8 when the grid stays large).
+int waves_16bit(int64_t n_bh, int64_t seq_q, int64_t head_dim) {
+#ifdef FA_FORCE_NW16
+  (void)n_bh; (void)seq_q; (void)head_dim;
+  return FA_FORCE_NW16;
+#else
+  if (head_dim > 128) return 4;
+  return n_bh * ((seq_q + 255) / 256) >= 1024 ? 8 : 4;
+#endif
+}
+
 template <typename T>
 fa_status_t launch_16bit(fa::FwdArgs& a, int64_t head_dim, void* stream) {
-#ifdef FA_FORCE_NW16
-  return launch_16bit_nw<T, FA_FORCE_NW16>(a, head_dim, stream);
-#else
-  const int64_t wg8 = (int64_t)a.n_bh * ((a.seq_q + 255) / 256);
-  if (wg8 >= 1024) return launch_16bit_nw<T, 8>(a, head_dim, stream);
+  if (waves_16bit(a.n_bh, a.seq_q, head_dim) == 8) return launch_16bit_nw<T, 8>(a, head_dim, stream);
   return launch_16bit_nw<T, 4>(a, head_dim, stream);
-#endif
+}
+
+// Key splitting: about one workgroup per CU, each split keeping at least
+// eight 64-key tiles (a workgroup's prologue and epilogue cost several
+// microseconds, so short shares do not pay), at most 16 splits.
+int choose_splits(int64_t n_bh, int64_t seq_q, int64_t seq_k, int64_t head_dim, int causal) {
+  const int64_t rows = 32 * waves_16bit(n_bh, seq_q, head_dim);
+  const int64_t grid = n_bh * ((seq_q + rows - 1) / rows);
+  if (grid <= 0 || grid >= 256) return 1;
+  const int64_t keys = causal ? std::min(seq_k, seq_q) : seq_k;  // longest key range of a tile
+  const int64_t tiles = (keys + 63) / 64;
+  int64_t s = (256 + grid - 1) / grid;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 8));
+  return (int)std::min<int64_t>(s, 16);
+}
+
+size_t splitk_workspace_bytes(int64_t n_bh, int64_t seq_q, int64_t head_dim, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)splits * (size_t)n_bh * (size_t)seq_q * (size_t)(head_dim + 1) * sizeof(float);
+}
+
+template <typename T>
+fa_status_t launch_combine(const fa::FwdArgs& a, void* stream) {
+  const int64_t rows = (int64_t)a.n_bh * a.seq_q;
+  fa::FwdArgs c = a;
+  void* params[] = {&c};
+  const void* kernel = a.n_splits <= 2   ? reinterpret_cast<const void*>(fa::fa_fwd_combine<T, 2>)
+                       : a.n_splits <= 4 ? reinterpret_cast<const void*>(fa::fa_fwd_combine<T, 4>)
+                       : a.n_splits <= 8 ? reinterpret_cast<const void*>(fa::fa_fwd_combine<T, 8>)
+                                         : reinterpret_cast<const void*>(fa::fa_fwd_combine<T, 16>);
+  hipError_t e = hipLaunchKernel(kernel,
+                                 dim3((unsigned)((rows + 31) / 32)), dim3(256), params, 0,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 fa_status_t launch_f32(fa::FwdArgs& a, int64_t head_dim, void* stream) {
@@ -171,15 +212,14 @@ fa_status_t launch_bwd_16bit(const fa::BwdArgs& a, int64_t head_dim, void* strea
   return launch_bwd_dp<T, 128>(a, stream);
 }
 
-}  // namespace
 
-extern "C" {
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
-                   fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
-                   float sm_scale, int causal, fa_dtype_t dtype, void* stream) {
-  g_last_error.clear();
+// Shared by fa_fwd (splits == 1, no workspace) and fa_fwd_splitk.
+fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                     fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
+                     float sm_scale, int causal, fa_dtype_t dtype, int splits, void* workspace,
+                     size_t workspace_bytes, bool split_api, void* stream) {
   if (batch < 0 || heads < 0 || seq_q < 0)
     return fail(FA_ERR_SHAPE, "batch, heads and seq_q must be >= 0");
   if (seq_k < 1) return fail(FA_ERR_SHAPE, "seq_k must be >= 1 (softmax over no keys)");
@@ -200,6 +240,12 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if ((s = check_strides("v", v_st, mult)) != FA_OK) return s;
   if ((s = check_strides("o", o_st, mult)) != FA_OK) return s;
   if (!std::isfinite(sm_scale)) return fail(FA_ERR_SCALE, "sm_scale must be finite");
+  if (split_api) {
+    if (splits < 0 || splits > fa::kMaxSplits)
+      return fail(FA_ERR_WORKSPACE, "num_splits %d outside 0..%d", splits, fa::kMaxSplits);
+    if (splits == 0) splits = f32 ? 1 : choose_splits(batch * heads, seq_q, seq_k, head_dim, causal);
+    if (f32 && splits > 1) return fail(FA_ERR_DTYPE, "key splitting needs bf16 or fp16 inputs");
+  }
   // an empty problem touches no memory, so its pointers may be NULL
   if (batch == 0 || heads == 0 || seq_q == 0) return FA_OK;
   if (!q || !k || !v || !o) return fail(FA_ERR_NULL, "q, k, v and o must be non-NULL");
@@ -207,6 +253,13 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (!aligned(q, align) || !aligned(k, align) || !aligned(v, align) || !aligned(o, align))
     return fail(FA_ERR_LAYOUT, "q, k, v and o must be %d-byte aligned", (int)align);
   if (lse && !aligned(lse, 4)) return fail(FA_ERR_LAYOUT, "lse must be 4-byte aligned");
+  const size_t need = splitk_workspace_bytes(batch * heads, seq_q, head_dim, splits);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_WORKSPACE, "a workspace of %zu bytes is needed", need);
+    if (!aligned(workspace, 256)) return fail(FA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  }
 
   fa::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -222,11 +275,59 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   a.c = std::fmax(std::fabs(sm_scale) * fa::kLog2e, 1e-30f);
   a.neg_scale = sm_scale < 0.f ? 1 : 0;
   a.causal = causal ? 1 : 0;
+  a.n_splits = splits;
+  if (splits > 1) {
+    a.part_o = (float*)workspace;
+    a.part_lse = a.part_o + (size_t)splits * (size_t)(batch * heads) * (size_t)seq_q * (size_t)head_dim;
+  }
+  fa_status_t st;
   switch (dtype) {
-    case FA_DTYPE_BF16: return launch_16bit<__bf16>(a, head_dim, stream);
-    case FA_DTYPE_F16: return launch_16bit<_Float16>(a, head_dim, stream);
+    case FA_DTYPE_BF16:
+      st = launch_16bit<__bf16>(a, head_dim, stream);
+      if (st == FA_OK && splits > 1) st = launch_combine<__bf16>(a, stream);
+      return st;
+    case FA_DTYPE_F16:
+      st = launch_16bit<_Float16>(a, head_dim, stream);
+      if (st == FA_OK && splits > 1) st = launch_combine<_Float16>(a, stream);
+      return st;
     default: return launch_f32(a, head_dim, stream);
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                   fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
+                   float sm_scale, int causal, fa_dtype_t dtype, void* stream) {
+  g_last_error.clear();
+  return fwd_impl(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_st, o_st,
+                  sm_scale, causal, dtype, 1, nullptr, 0, false, stream);
+}
+
+int fa_fwd_splitk_choose(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                         int64_t head_dim, int causal) {
+  if (batch <= 0 || heads <= 0 || seq_q <= 0 || seq_k <= 0 || head_dim <= 0) return 1;
+  return choose_splits(batch * heads, seq_q, seq_k, head_dim, causal);
+}
+
+size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int64_t head_dim,
+                               int num_splits) {
+  if (batch <= 0 || heads <= 0 || seq_q <= 0 || head_dim <= 0) return 0;
+  return splitk_workspace_bytes(batch * heads, seq_q, head_dim, num_splits);
+}
+
+fa_status_t fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                          int64_t head_dim, fa_strides_t q_st, fa_strides_t k_st,
+                          fa_strides_t v_st, fa_strides_t o_st, float sm_scale, int causal,
+                          fa_dtype_t dtype, int num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return fwd_impl(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_st, o_st,
+                  sm_scale, causal, dtype, num_splits, workspace, workspace_bytes, true, stream);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -299,6 +400,7 @@ const char* fa_status_string(fa_status_t s) {
     case FA_ERR_LAYOUT: return "FA_ERR_LAYOUT";
     case FA_ERR_HIP: return "FA_ERR_HIP";
     case FA_ERR_SCALE: return "FA_ERR_SCALE";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
   }
   return "FA_ERR_UNKNOWN";
 }

@@ -78,13 +78,19 @@ struct FwdArgs {
   int32_t neg_scale;  // sm_scale < 0: Q is negated in registers
   int32_t causal;
   int32_t xcd_remap;  // n_bh % 8 == 0: keep one (batch, head) on one XCD
+  // key splitting: n_splits workgroups share each query tile's key tiles and
+  // write fp32 partials (O_r normalised by its own row sum, lse_r; -inf and 0
+  // for rows that see no key of the share) that fa_fwd_combine merges
+  int32_t n_splits;   // 1: no splitting, O and lse written directly
+  float* part_o;      // [n_splits, n_bh, seq_q, head_dim]
+  float* part_lse;    // [n_splits, n_bh, seq_q]
 };
 
-// Map the linear workgroup id to (batch*head, query tile).  Workgroups are
-// handed to the 8 XCDs round-robin, so ids with the same residue mod 8 share
-// an XCD and its L2; all tiles of one (batch, head) get the same residue.
-// Causal: heaviest (last) query tiles are dispatched first.
-__device__ inline void map_workgroup(const FwdArgs& a, int wg, int& bh, int& qt) {
+// Map the linear workgroup id to (batch*head, query tile, key split).
+// Workgroups are handed to the 8 XCDs round-robin, so ids with the same
+// residue mod 8 share an XCD and its L2; all tiles of one (batch, head) get
+// the same residue.  Causal: heaviest (last) query tiles are dispatched first.
+__device__ inline void map_workgroup(const FwdArgs& a, int wg, int& bh, int& qt, int& split) {
   int rank;
   if (a.xcd_remap) {
     const int per = a.n_bh >> 3;
@@ -95,6 +101,8 @@ __device__ inline void map_workgroup(const FwdArgs& a, int wg, int& bh, int& qt)
     bh = wg % a.n_bh;
     rank = wg / a.n_bh;
   }
+  split = rank % a.n_splits;
+  rank /= a.n_splits;
   qt = a.causal ? a.n_qtiles - 1 - rank : rank;
 }
 
@@ -230,8 +238,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   const int l32 = lane & 31;   // query column owned by this lane
   const int hi = lane >> 5;    // which half of the 32x32 result rows
 
-  int bh, qt;
-  map_workgroup(a, blockIdx.x, bh, qt);
+  int bh, qt, split;
+  map_workgroup(a, blockIdx.x, bh, qt, split);
   const int b = bh / a.heads, h = bh - b * a.heads;
 
   const T* qg = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
@@ -242,13 +250,16 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   const int q0 = qt * G::BM;
   const int qw = q0 + wave * 32;        // first query row of this wave
   const int my_q = qw + l32;            // query row of this lane
-  const int wave_last = min(qw + 31, a.seq_q - 1);
   const bool wave_live = qw < a.seq_q;
   const int wave_rows = wave_live ? min(32, a.seq_q - qw) : 0;
 
-  // keys this workgroup must visit (causal: up to its last real query)
+  // keys this workgroup must visit (causal: up to its last real query), and
+  // with key splitting its share [t0, t1) of those 64-key tiles
   const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + G::BM)) : a.seq_k;
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  const int n_all = (kv_end + BN - 1) / BN;
+  const int chunk = (n_all + a.n_splits - 1) / a.n_splits;
+  const int t0 = min(n_all, split * chunk);
+  const int t1 = min(n_all, t0 + chunk);
 
   // ---- resident Q fragment: B operand of S^T, lane = (query l32, dims 8*hi..+7 of each step)
   frag qf[KSTEPS];
@@ -287,7 +298,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     const int key0 = j * BN;
     const int rows = min(BN, a.seq_k - key0);
     const auto rk = make_rsrc(kg + (int64_t)key0 * a.k_ss, (rows - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2);
-    FA_LDS char* kb = lds + (j & 1) * G::STAGE;
+    FA_LDS char* kb = lds + ((j - t0) & 1) * G::STAGE;
 #pragma unroll
     for (int n = 0; n < G::KPER; ++n)
       if (wave + NW * n < G::KINSTR)
@@ -298,7 +309,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     const int key0 = j * BN;
     const int rows = min(BN, a.seq_k - key0);
     const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
-    FA_LDS char* vb = lds + (j & 1) * G::STAGE + G::KBYTES;
+    FA_LDS char* vb = lds + ((j - t0) & 1) * G::STAGE + G::KBYTES;
 #pragma unroll
     for (int n = 0; n < G::VPER; ++n)
       if (wave + NW * n < G::VINSTR)
@@ -398,7 +409,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     }
   };
 
-  // One pipelined step for tile t (parity = t & 1, known at compile time):
+  // One pipelined step for tile t (parity = (t - t0) & 1, known at compile time):
   // the MFMAs of S(t+1) are issued in the same basic block as the softmax
   // VALU work of tile t, so the matrix pipe stays busy while P(t) is formed;
   // then P(t) V(t).  K runs one tile ahead of V in LDS: during step t the
@@ -408,8 +419,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   auto step = [&](int t, auto parity, auto has_next, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     constexpr int P = decltype(parity)::value;
     stats(t, cur);
-    if (t + 2 < n_tiles) issue_k(t + 2);
-    if (t + 1 < n_tiles) issue_v(t + 1);
+    if (t + 2 < t1) issue_k(t + 2);
+    if (t + 1 < t1) issue_v(t + 1);
     uint32_t pk[2][8];
     if constexpr (decltype(has_next)::value) scores(1 - P, nxt);
     probs(cur, pk);
@@ -421,20 +432,20 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   using No = std::integral_constant<bool, false>;
 
   f32x16_t sa[2], sb[2];
-  if (n_tiles > 0) {
-    issue_k(0);
-    issue_v(0);
-    if (n_tiles > 1) issue_k(1);
+  if (t1 > t0) {
+    issue_k(t0);
+    issue_v(t0);
+    if (t0 + 1 < t1) issue_k(t0 + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     scores(0, sa);
-    __syncthreads();  // K(0) consumed by all waves before step 0 loads K(2) over it
-    int t = 0;
-    for (; t + 2 < n_tiles; t += 2) {
+    __syncthreads();  // K(t0) consumed by all waves before the first step loads K(t0+2) over it
+    int t = t0;
+    for (; t + 2 < t1; t += 2) {
       step(t, Even{}, Yes{}, sa, sb);
       step(t + 1, Odd{}, Yes{}, sb, sa);
     }
-    if (t + 1 < n_tiles) {
+    if (t + 1 < t1) {
       step(t, Even{}, Yes{}, sa, sb);
       step(t + 1, Odd{}, No{}, sb, sa);
     } else {
@@ -445,6 +456,30 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
   if (!wave_live) return;
   const float l_tot = xlane_sum(l_run);
+  if (a.n_splits > 1) {
+    // fp32 partials of this key share; a row that saw none of its keys has
+    // l = 0 and gets O_r = 0, lse_r = -inf (weight 0 in the merge)
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? 1.0f / l_tot : 0.f;
+    const int64_t row0 = ((int64_t)split * a.n_bh + bh) * a.seq_q + qw;
+    const auto rp = make_rsrc(a.part_o + row0 * a.head_dim, wave_rows * a.head_dim * 4);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hi;
+        const uint32_t off = (d0 < a.head_dim && l32 < wave_rows)
+                                 ? (uint32_t)((l32 * a.head_dim + d0) * 4) : kOutOfRange;
+        const u32x4_t w = {__float_as_uint(acc[db][4 * g + 0] * inv),
+                           __float_as_uint(acc[db][4 * g + 1] * inv),
+                           __float_as_uint(acc[db][4 * g + 2] * inv),
+                           __float_as_uint(acc[db][4 * g + 3] * inv)};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rp, off, 0, 0);
+      }
+    if (hi == 0 && l32 < wave_rows)
+      a.part_lse[row0 + l32] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    return;
+  }
   const float inv = 1.0f / l_tot;
   const int32_t onrec = (wave_rows - 1) * (int32_t)a.o_ss * 2 + a.head_dim * 2;
   const auto ro = make_rsrc(og + (int64_t)qw * a.o_ss, onrec);
@@ -497,8 +532,8 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int bh, qt;
-  map_workgroup(a, blockIdx.x, bh, qt);
+  int bh, qt, split;
+  map_workgroup(a, blockIdx.x, bh, qt, split);
   const int b = bh / a.heads, h = bh - b * a.heads;
   const float* qg = (const float*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
   const float* kg = (const float*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
@@ -619,6 +654,62 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(FwdArgs a) {
     if (hi == 0 && a.lse != nullptr)
       a.lse[(int64_t)bh * a.seq_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the key-split partials:  lse = log sum_r exp(lse_r),
+// O = sum_r exp(lse_r - lse) O_r  (the lse-weighted combination that also
+// merges two online-softmax states), rounded once into the output type.
+// 8 lanes per row, each covering dims 8*sub + 64*c .. +7.
+// ---------------------------------------------------------------------------
+constexpr int kMaxSplits = 16;
+
+// SMAX: a compile-time bound on the split count (2, 4, 8 or 16), so every
+// partial of a row is loaded with straight-line, independent loads.
+template <typename T, int SMAX>
+__global__ __launch_bounds__(256) void fa_fwd_combine(FwdArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 32 + (tid >> 3);
+  const int sub = tid & 7;
+  const int64_t rows = (int64_t)a.n_bh * a.seq_q;
+  if (row >= rows) return;
+  const int S = a.n_splits;
+  // all partial lse values at once (independent loads in flight together)
+  float l[SMAX];
+#pragma unroll
+  for (int r = 0; r < SMAX; ++r)
+    l[r] = r < S ? a.part_lse[(int64_t)r * rows + row] : -INFINITY;
+  float m = l[0];
+#pragma unroll
+  for (int r = 1; r < SMAX; ++r) m = fmaxf(m, l[r]);
+  float den = 0.f;
+#pragma unroll
+  for (int r = 0; r < SMAX; ++r) {
+    l[r] = __expf(l[r] - m);  // weight before normalisation (0 for absent splits)
+    den += l[r];
+  }
+  const float inv = 1.0f / den;
+  const float lse = m + __logf(den);
+  const int bh = (int)(row / a.seq_q), i = (int)(row - (int64_t)bh * a.seq_q);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  T* orow = (T*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)i * a.o_ss;
+  typedef T t8 __attribute__((ext_vector_type(8)));
+  typedef float f8 __attribute__((ext_vector_type(8)));
+  for (int d0 = sub * 8; d0 < a.head_dim; d0 += 64) {
+    f8 part[SMAX];
+#pragma unroll
+    for (int r = 0; r < SMAX; ++r)
+      part[r] = r < S ? *(const f8*)(a.part_o + ((int64_t)r * rows + row) * a.head_dim + d0)
+                      : (f8){};
+    f8 acc = {};
+#pragma unroll
+    for (int r = 0; r < SMAX; ++r) acc += (l[r] * inv) * part[r];
+    t8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (T)acc[e];
+    *(t8*)(orow + d0) = out;
+  }
+  if (sub == 0 && a.lse != nullptr) a.lse[row] = lse;
 }
 
 }  // namespace fa

@@ -79,6 +79,16 @@ WORKLOADS = {
                    stress_frac=0.01, stress_factor=8.0),
 }
 
+# Short-query / cross-attention shapes of the form the triton issue's test
+# matrix uses (few query rows against 4096 keys, [seq, heads, d], fp16):
+# timing cases for the key-split forward, not target configurations.
+EXTRA_WORKLOADS = {
+    "short100": Workload("fp16 s_q=100 s_k=4096 h=12 d=64 seq-heads-d, non-causal", "fp16",
+                         "shd", 1, 12, 100, 4096, 64, 1.0, 0.5, False, seed=41),
+    "short10": Workload("fp16 s_q=10 s_k=4096 h=12 d=64 seq-heads-d, non-causal", "fp16",
+                        "shd", 1, 12, 10, 4096, 64, 1.0, 0.5, False, seed=42),
+}
+
 _CHUNK = 1 << 22
 
 
@@ -146,7 +156,7 @@ class Inputs:
 def make_inputs(w, seq_q=None, seq_k=None):
     """Draw the inputs of workload ``w`` (a Workload or a key of WORKLOADS)."""
     if isinstance(w, str):
-        w = WORKLOADS[w]
+        w = WORKLOADS[w] if w in WORKLOADS else EXTRA_WORKLOADS[w]
     rng = np.random.default_rng(w.seed)
     q = _draw(rng, w.shape("q"), w.std, w.dtype)
     k = _draw(rng, w.shape("k"), w.std, w.dtype)
