@@ -138,9 +138,13 @@ struct Mfma<_Float16> {
   }
 };
 
-// Smallest stride >= min_bytes that is congruent to `residue` modulo 256.
-constexpr int pad_to_residue(int min_bytes, int residue) {
-  return ((min_bytes - residue + 255) / 256) * 256 + residue;
+// Smallest row stride (bytes, multiple of 16, >= min_bytes) congruent to 64
+// or 192 modulo 256: then the 4 rows x 64 bytes that 32 lanes of a
+// transposing read gather fall into disjoint bank windows.
+constexpr int tr_row_stride(int min_bytes) {
+  int st = (min_bytes + 15) / 16 * 16;
+  while (st % 256 != 64 && st % 256 != 192) st += 16;
+  return st;
 }
 
 // ---------------------------------------------------------------------------
@@ -201,9 +205,9 @@ struct Tile16 {
   // K rows: stride = 16 (mod 256) bytes, so the 32 lanes reading one 16-byte
   // chunk of 32 consecutive rows fall on distinct bank groups.
   static constexpr int KROW = D * 2 + 16;
-  // V rows: stride = 64 (mod 256) bytes, so the 4 rows x 32 bytes gathered by
-  // each 16-lane group of a transposing read fall on distinct banks.
-  static constexpr int VROW = pad_to_residue(DBLK * 64, 64);
+  // V rows: stride = 64 or 192 (mod 256) bytes, so the rows gathered by a
+  // transposing read fall on distinct banks.
+  static constexpr int VROW = tr_row_stride(DBLK * 64);
   static constexpr int KSLOTS = KROW / 16;     // 16-byte LDS slots per K row (incl. padding)
   static constexpr int VSLOTS = VROW / 16;
   static constexpr int KINSTR = BN * KSLOTS / 64;  // wave-wide 1 KiB loads per K tile
