@@ -16,7 +16,9 @@ Prints one JSON line:
 
 Other modes:
   --workload c2|c3|c4   time another workload (not the default line); also
-                        short100 / short10 (few queries against 4096 keys)
+                        short100 / short10 (few queries against 4096 keys) and
+                        c5_e5m2 (the default workload in float8 e5m2, V passed
+                        key-major; roofline against the dense fp8 MFMA peak)
   --splits S            forward through fa_fwd_splitk with S key splits (0: the
                         library's choice)
   --copy-calib          also run a plain device copy of 1 GiB (for counter
@@ -40,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (1 GPU)"
 KERNEL_SOURCES = ["tiled_attention_04_amd/csrc/fa_fwd_kernels.hpp",
                   "tiled_attention_04_amd/csrc/fa_api.hip"]
@@ -186,7 +189,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5",
-                    choices=["c2", "c3", "c4", "c5", "short100", "short10"])
+                    choices=["c2", "c3", "c4", "c5", "short100", "short10", "c5_e5m2"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-pmc", default=None)
@@ -222,9 +225,17 @@ def main():
         if w.dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
                 torch.bfloat16).to(dev)
+        if w.dtype == "e5m2":
+            return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e5m2).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    q, k = up(inp.q), up(inp.k)
+    if w.dtype == "e5m2":
+        # the fp8 path takes V key-major: [B, H, D, Sk] (Sk is a multiple of 16 here)
+        v = up(np.transpose(inp.v, (0, 1, 3, 2)))
+    else:
+        v = up(inp.v)
+    peak = PEAK_FP8_TFLOPS if w.dtype == "e5m2" else PEAK_BF16_TFLOPS
     layout = "shd" if w.layout == "shd" else "bhsd"
     o = torch.empty_like(q)
     lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
@@ -306,9 +317,9 @@ def main():
                    "seq_q": w.seq_q,
                    "seq_k": w.seq_k, "head_dim": w.head_dim, "causal": w.causal,
                    "sm_scale": w.sm_scale, "flops_per_step": flops},
-        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms_avg": round(ms_avg, 5),
                      "kernel_ms_min": round(per_launch[0], 5)},
         "context": {"rtx3090_unfused_per_call": CONTEXT_RTX3090},

@@ -29,7 +29,9 @@ extern "C" {
 typedef enum {
   FA_DTYPE_F32 = 0,  /* IEEE binary32; scores and P stay fp32 (fp32 MFMA) */
   FA_DTYPE_F16 = 1,  /* IEEE binary16; P rounded to fp16 for the P.V product */
-  FA_DTYPE_BF16 = 2  /* bfloat16;      P rounded to bf16 for the P.V product */
+  FA_DTYPE_BF16 = 2, /* bfloat16;      P rounded to bf16 for the P.V product */
+  FA_DTYPE_E5M2 = 3  /* float8 e5m2 (OCP: the upper byte of an IEEE binary16), fa_fwd
+                        only: V key-major, P and O rounded to e5m2 (see fa_fwd) */
 } fa_dtype_t;
 
 typedef enum {
@@ -64,6 +66,17 @@ typedef struct {
  *   lse  [batch, heads, seq_q] fp32, contiguous, natural log (output);
  *        may be NULL, in which case it is not written.
  *
+ * FA_DTYPE_E5M2 (the fp8 path of "Understanding Triton Tutorials Part 2",
+ * section "Fused Attention 2": all of q, k, v, o in float8 e5m2, v stored
+ * transposed): head_dim a multiple of 16 up to 128; v is passed key-major --
+ * v_st.seq == 1 and v_st.dim, the distance between the key rows of two
+ * dims, a multiple of 16 and >= seq_k; other strides multiples of 16.  Keys
+ * between seq_k and the next multiple of 16 are read from the row (their P
+ * is 0), so they must hold finite values.  P is rounded to e5m2 before P.V
+ * and O is rounded to e5m2; softmax and accumulation across MFMAs stay fp32
+ * (inside one e5m2 MFMA the products are summed in groups of 8, each kept to
+ * 13 bits below its group's largest product).  Base pointers 16-byte aligned.
+ *
  * Semantics per query row i of each (batch, head):
  *   visible keys A(i) = { j < seq_k : causal == 0 or j <= i }   (top-left
  *   alignment when seq_q != seq_k, so key 0 is always visible);
@@ -82,16 +95,16 @@ typedef struct {
  *   batch, heads, seq_q < 0, seq_k < 1, or any size, the grid or an index
  *   that would exceed int32                      -> FA_ERR_SHAPE
  *   dtype unknown                                -> FA_ERR_DTYPE
- *   head_dim < 1, > 256, or not a multiple of 8 (f16/bf16) or 4 (f32)
- *                                                -> FA_ERR_HEAD_DIM
+ *   head_dim < 1, > 256, or not a multiple of 8 (f16/bf16) or 4 (f32);
+ *   e5m2: > 128 or not a multiple of 16            -> FA_ERR_HEAD_DIM
  *   a dim stride != 1, any negative stride, a seq stride >= 2^24 elements,
- *   a batch/head/seq stride not a multiple of 8 elements (f16/bf16)
- *                                                -> FA_ERR_LAYOUT
+ *   a batch/head/seq stride not a multiple of 8 elements (f16/bf16) or of
+ *   16 (e5m2); e5m2 v not key-major as above     -> FA_ERR_LAYOUT
  *   sm_scale NaN or infinite                     -> FA_ERR_SCALE
  *   batch, heads or seq_q == 0                   -> FA_OK, nothing launched
  *                                                   (pointers may be NULL)
  *   q/k/v/o NULL                                 -> FA_ERR_NULL
- *   a base pointer not 16-byte aligned (f16/bf16) or 4-byte aligned (f32),
+ *   a base pointer not 16-byte aligned (f16/bf16/e5m2) or 4-byte aligned (f32),
  *   lse not 4-byte aligned                       -> FA_ERR_LAYOUT
  * A failed launch returns FA_ERR_HIP.  On any non-OK return nothing has been
  * enqueued and fa_last_error() describes the problem.
@@ -119,8 +132,9 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
  *                    fa_fwd_splitk_workspace(batch, heads, seq_q, head_dim,
  *                    splits) bytes (fp32 partials); contents are overwritten
  *   workspace_bytes  its size.
- * Key splitting needs bf16/fp16 (fp32 with num_splits > 1 -> FA_ERR_DTYPE);
- * num_splits outside 0..16 or a missing/misaligned/short workspace ->
+ * Key splitting needs bf16/fp16 (fp32 or e5m2 with num_splits > 1 ->
+ * FA_ERR_DTYPE; num_splits outside 0..16 -> FA_ERR_WORKSPACE; both checked
+ * right after the dtype); a missing/misaligned/short workspace ->
  * FA_ERR_WORKSPACE (checked after the fa_fwd checks, before any HIP call).
  * O is rounded once, after the merge.  Two calls that share a workspace on
  * different streams race.
@@ -176,8 +190,8 @@ size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int6
  * synchronisation).  No output may overlap an input.
  *
  * Validation on the host before any HIP call: the fa_fwd rules for sizes,
- * strides and sm_scale over all eight tensors; dtype FA_DTYPE_F32
- * -> FA_ERR_DTYPE; head_dim > 128 -> FA_ERR_HEAD_DIM; batch or heads == 0
+ * strides and sm_scale over all eight tensors; dtype FA_DTYPE_F32 or
+ * FA_DTYPE_E5M2 -> FA_ERR_DTYPE; head_dim > 128 -> FA_ERR_HEAD_DIM; batch or heads == 0
  * -> FA_OK with nothing launched; k, v, dk, dv NULL, or (seq_q > 0) q, o,
  * dout, lse, delta, dq NULL -> FA_ERR_NULL; a tensor not 16-byte aligned or
  * lse/delta not 4-byte aligned -> FA_ERR_LAYOUT.  If a launch fails

@@ -12,7 +12,8 @@ import tiled_attention_04_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 S = fa.FaStrides
 CONTIG = S(64 * 128 * 16, 64 * 128, 64, 1)  # [b, h, s=128, d=64]
-BF16, F16, F32 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16, fa.FA_DTYPE_F32
+BF16, F16, F32, E5M2 = fa.FA_DTYPE_BF16, fa.FA_DTYPE_F16, fa.FA_DTYPE_F32, fa.FA_DTYPE_E5M2
+VT = S(2 * 64 * 128, 64 * 128, 1, 128)  # key-major V [b, h, d=64, s=128] (e5m2)
 P = 1 << 20  # a 16-byte-aligned fake address (never dereferenced: calls fail validation)
 
 
@@ -52,7 +53,7 @@ def call(q=P, k=P, v=P, o=P, lse=None, batch=1, heads=2, sq=128, sk=128, d=64, q
 @pytest.mark.parametrize("kwargs,code", [
     (dict(batch=-1), 2), (dict(heads=-3), 2), (dict(sq=-1), 2), (dict(sk=0), 2),
     (dict(sk=-5), 2), (dict(sq=1 << 31), 2), (dict(batch=1 << 20, heads=1 << 12), 2),
-    (dict(dtype=3), 3), (dict(dtype=-1), 3),
+    (dict(dtype=4), 3), (dict(dtype=-1), 3),
     (dict(d=0), 4), (dict(d=257), 4), (dict(d=12), 4), (dict(d=6, dtype=F32), 4),
     (dict(qs=S(0, 0, 64, 2)), 5), (dict(ks=S(0, -64, 64, 1)), 5), (dict(vs=S(0, 0, 68, 1)), 5),
     (dict(os_=S(0, 0, 1 << 24, 1)), 5), (dict(q=P + 8), 5), (dict(o=P + 2, dtype=F32), 5),
@@ -79,6 +80,24 @@ def test_fp32_accepts_unaligned_strides():
     assert rc == 1
 
 
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(d=136), 4), (dict(d=256), 4), (dict(d=24), 4), (dict(d=8), 4),
+    (dict(vs=CONTIG), 5), (dict(vs=S(0, 0, 1, 112)), 5), (dict(vs=S(0, 0, 1, 136)), 5),
+    (dict(vs=S(8, 0, 1, 128)), 5), (dict(vs=S(0, 0, 1, 1 << 24)), 5),
+    (dict(qs=S(0, 0, 72, 1)), 5), (dict(ks=S(0, 8, 64, 1)), 5), (dict(q=P + 8), 5),
+    (dict(v=P + 4), 5),
+    (dict(q=None), 1), (dict(d=16, q=None), 1), (dict(d=128, q=None, vs=S(0, 0, 1, 144)), 1),
+])
+def test_e5m2_validation_errors(kwargs, code):
+    # q, k, o row-major with 16-byte rows; V key-major (seq stride 1, dim
+    # stride a multiple of 16 that holds seq_k keys); head_dim 16..128 by 16
+    args = dict(vs=VT, dtype=E5M2)
+    args.update(kwargs)
+    rc = call(**args)
+    assert rc == code, (kwargs, rc, fa.last_error())
+    assert fa.last_error() != ""
+
+
 def call_bwd(q=P, k=P, v=P, o=P, do=P, lse=P, delta=P, dq=P, dk=P, dv=P, batch=1, heads=2,
              sq=128, sk=128, d=64, sts=None, scale=0.125, causal=0, dtype=BF16):
     st = dict(q=CONTIG, k=CONTIG, v=CONTIG, o=CONTIG, do=CONTIG, dq=CONTIG, dk=CONTIG, dv=CONTIG)
@@ -90,7 +109,7 @@ def call_bwd(q=P, k=P, v=P, o=P, do=P, lse=P, delta=P, dq=P, dk=P, dv=P, batch=1
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(batch=-1), 2), (dict(sq=-2), 2), (dict(sk=0), 2), (dict(sq=1 << 31), 2),
-    (dict(dtype=F32), 3), (dict(dtype=5), 3),
+    (dict(dtype=F32), 3), (dict(dtype=E5M2), 3), (dict(dtype=5), 3),
     (dict(d=0), 4), (dict(d=136), 4), (dict(d=256), 4), (dict(d=60), 4),
     (dict(sts={"do": S(0, 0, 64, 2)}), 5), (dict(sts={"dk": S(0, -64, 64, 1)}), 5),
     (dict(sts={"dv": S(0, 0, 68, 1)}), 5), (dict(sts={"o": S(0, 0, 1 << 24, 1)}), 5),
@@ -128,7 +147,8 @@ def call_splitk(splits=2, ws=P, ws_bytes=1 << 30, dtype=BF16, **kw):
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(splits=-1), 8), (dict(splits=17), 8), (dict(ws=None), 8), (dict(ws=P + 16), 8),
-    (dict(ws_bytes=1000), 8), (dict(splits=2, dtype=F32), 3), (dict(sk=0), 2),
+    (dict(ws_bytes=1000), 8), (dict(splits=2, dtype=F32), 3), (dict(splits=2, dtype=E5M2), 3),
+    (dict(sk=0), 2),
     (dict(q=None), 1),
 ])
 def test_splitk_validation_errors(kwargs, code):

@@ -1,0 +1,233 @@
+"""GPU parity of the float8 e5m2 forward (fa_fwd with FA_DTYPE_E5M2).
+
+The fp8 path of "Understanding Triton Tutorials Part 2", section "Fused
+Attention 2": Q, K, V and O in e5m2, V handed over key-major, P rounded to
+e5m2 before the P V product.  The oracle computes the exact softmax attention
+of the e5m2-valued inputs in double.
+
+The e5m2 MFMA's own arithmetic (measured with an in-bounds probe of
+v_mfma_f32_32x32x64_f8f6f4): the 64 products of one instruction are summed in
+groups of 8, each product truncated toward zero to a multiple of 2^-13 times
+the leading power of two of its group's largest product, and the group sums
+then enter the fp32 accumulator (rounding ~2^-24).  One instruction therefore
+errs by less than G |sum| with G = 7 * 2^-13 + 2^-20 relative to the sum of
+the absolute products.  Q K^T with integer entries of magnitude <= 2 is exact.
+
+Two kinds of check (the target states no fp8 tolerance, so both follow from
+that arithmetic):
+
+* exact cases -- integer scores (``synth.make_integer_score_inputs``) with a
+  scale of +-ln 2, or a scale of 0: every softmax weight relative to the row
+  maximum is an exact power of two, which e5m2 holds, so P is rounded
+  without error.  The kernel's O must then be the e5m2 rounding (RNE) of a
+  value within w = 1e-4 |O| + 1.1 G O_abs of the exact O, where O_abs is the
+  attention output over |V| (the P V products' grouping error scales with
+  it); and since w is far below the e5m2 spacing for most elements, at most
+  2% of the elements may differ from RNE(O) at all.  A mistake in which key
+  meets which weight or dim shows here.
+* general Gaussian inputs -- a rigorous bound.  Scores err by at most
+  G sum_d |q_d k_d|, so with delta = |scale| G max_j sum_d |q_d k_jd| (visible
+  keys) every softmax weight is within a factor e^(+-2 delta) of the exact
+  one and lse within delta.  P is rounded with relative error <= 2^-3 (e5m2
+  has 3 significant bits) or absolute error <= 2^-17 (subnormals; l >= 1
+  relative to the running maximum), and P V adds its grouping error, so the
+  pre-rounding O is within
+      E1 = (e^(2 delta) - 1) O_abs + e^(2 delta) ((2^-3 + 1.2 G) O_abs + 2^-17 sum_j |v_j|)
+  of the exact O; rounding O to e5m2 adds <= 2^-3 (|O| + E1) + 2^-17.  Per
+  element |err| <= 1.02 (1.125 E1 + 0.125 |O| + 2^-17) + 1e-6, and the mean
+  error stays below half the mean bound (RNE errors average well inside it).
+lse: |err| <= delta + 1e-5 (1 + |lse|) (exact cases: delta = 0).
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+from tiled_attention_04_amd import synth  # noqa: E402
+from gpu_cases import say, sampled_rows  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+LN2 = float(np.float32(math.log(2.0)))  # the scale the C ABI receives
+G = 7 * 2.0 ** -13 + 2.0 ** -20  # relative error of one e5m2 MFMA (see above)
+
+
+def upload_e5m2(codes):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e5m2).cuda()
+
+
+def key_major(v_codes, layout, pad_to=None, pad_code=0x42):
+    """V codes [B,H,Sk,D] (or [Sk,H,D]) -> key-major [B,H,D,Sv] ([H,D,Sv]), the
+    keys past Sk filled with a finite code (0x42 = 3.0)."""
+    v = np.transpose(v_codes, (1, 0, 2))[None] if layout == "shd" else v_codes
+    B, H, S, D = v.shape
+    sv = pad_to if pad_to is not None else (S + 15) // 16 * 16
+    out = np.full((B, H, D, sv), pad_code, dtype=np.uint8)
+    out[..., :S] = np.transpose(v, (0, 1, 3, 2))
+    return out[0] if layout == "shd" else out
+
+
+def run_e5m2(inp, causal, sm_scale, pad_to=None):
+    import torch
+    import tiled_attention_04_amd as fa
+    w = inp.workload
+    layout = "shd" if w.layout == "shd" else "bhsd"
+    q, k = upload_e5m2(inp.q), upload_e5m2(inp.k)
+    vt = upload_e5m2(key_major(inp.v, w.layout, pad_to))
+    o, lse = fa.forward(q, k, vt, causal=causal, sm_scale=sm_scale, layout=layout)
+    torch.cuda.synchronize()
+    o_codes = o.view(torch.uint8).cpu().numpy()
+    if layout == "shd":
+        o_codes = np.transpose(o_codes, (1, 0, 2))[None]
+    return synth.widen(o_codes, "e5m2"), lse.double().cpu().numpy()
+
+
+def e5m2_value(x):
+    return synth.widen(synth.round_to_dtype(x, "e5m2"), "e5m2")
+
+
+def check_exact(name, o_gpu, lse_gpu, o_ref, o_abs, lse_ref):
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), f"{name}: non-finite"
+    w = 1e-4 * np.abs(o_ref) + 1.1 * G * o_abs
+    lo, hi = e5m2_value(o_ref - w), e5m2_value(o_ref + w)
+    ok = (o_gpu >= lo) & (o_gpu <= hi)
+    exact = e5m2_value(o_ref)
+    n_diff = int(np.sum(o_gpu != exact))
+    err_l = np.abs(lse_gpu - lse_ref)
+    msg = (f"{name}: {n_diff} of {o_gpu.size} O differ from RNE(O_exact), "
+           f"{int(np.sum(~ok))} outside the window; lse max {err_l.max():.3e}")
+    say(msg)
+    assert ok.all(), msg
+    assert n_diff <= 0.02 * o_gpu.size, msg
+    assert np.all(err_l <= 1e-5 * (1 + np.abs(lse_ref))), msg
+
+
+def bound(o_ref, o_abs, vsum_abs, delta):
+    grow = np.exp(2 * delta)
+    e1 = (grow - 1) * o_abs + grow * ((0.125 + 1.2 * G) * o_abs + 2.0 ** -17 * vsum_abs)
+    return 1.02 * (1.125 * e1 + 0.125 * np.abs(o_ref) + 2.0 ** -17) + 1e-6
+
+
+def check_bound(name, o_gpu, lse_gpu, o_ref, o_abs, vsum_abs, lse_ref, delta):
+    """delta: per row, broadcastable against lse (and O with a trailing axis)."""
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), f"{name}: non-finite"
+    err = np.abs(o_gpu - o_ref)
+    b = bound(o_ref, o_abs, vsum_abs, delta[..., None])
+    err_l = np.abs(lse_gpu - lse_ref)
+    tol_l = delta + 1e-5 * (1 + np.abs(lse_ref))
+    msg = (f"{name}: O max err/bound {np.max(err / b):.3f}, mean err {err.mean():.3e} "
+           f"vs mean bound {b.mean():.3e}; lse max err/bound {np.max(err_l / tol_l):.3f} "
+           f"(max delta {np.max(delta):.2e})")
+    say(msg)
+    assert np.all(err <= b), msg
+    assert err.mean() <= 0.5 * b.mean(), msg
+    assert np.all(err_l <= tol_l), msg
+
+
+def score_delta(q, k, sm_scale, causal, q_pos=None):
+    """|scale| G max over visible keys of sum_d |q_d k_d|, per query row.
+    q [..., R, D], k [..., Sk, D]; q_pos: query positions (default 0..R-1)."""
+    s_abs = np.abs(q) @ np.swapaxes(np.abs(k), -1, -2)
+    if causal:
+        pos = np.arange(q.shape[-2]) if q_pos is None else q_pos
+        s_abs = np.where(np.arange(k.shape[-2])[None, :] > pos[:, None], 0.0, s_abs)
+    return abs(sm_scale) * G * s_abs.max(axis=-1)
+
+
+def oracle_parts(inp, sm_scale, causal):
+    q, k, v = inp.as_bhsd_f64("q"), inp.as_bhsd_f64("k"), inp.as_bhsd_f64("v")
+    o_ref, lse_ref = oracle.forward(q, k, v, sm_scale, causal)
+    o_abs, _ = oracle.forward(q, k, np.abs(v), sm_scale, causal)
+    vsum = np.abs(v).sum(axis=2, keepdims=True)
+    return o_ref, o_abs, vsum, lse_ref, score_delta(q, k, sm_scale, causal)
+
+
+def exact_case(name, layout, B, H, Sq, Sk, D, causal, scale, seed, pad_to=None, integer=True):
+    w = synth.custom(name, "e5m2", layout, B, H, Sq, Sk, D, causal=causal, seed=seed)
+    inp = synth.make_integer_score_inputs(w) if integer else synth.make_inputs(w)
+    say(f"[gpu] e5m2 exact {name}: B={B} H={H} Sq={Sq} Sk={Sk} D={D} causal={causal} "
+        f"scale={scale} pad_to={pad_to}")
+    o, lse = run_e5m2(inp, causal, scale, pad_to)
+    o_ref, o_abs, _, lse_ref, _ = oracle_parts(inp, scale, causal)
+    check_exact(name, o, lse, o_ref, o_abs, lse_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("head_dim", [16, 48, 64, 80, 128])
+def test_e5m2_exact_ragged(causal, head_dim):
+    # several 64-key tiles, a key count that is no multiple of 16, a query
+    # count that is no multiple of 32
+    exact_case(f"d{head_dim}", "bhsd", 2, 3, 150, 333, head_dim, causal, LN2, seed=300 + head_dim)
+
+
+@pytest.mark.parametrize("scale", [-LN2, 0.0])
+def test_e5m2_exact_scales(scale):
+    # a negative scale flips the sign of every score; scale 0 gives equal
+    # weights over the visible keys (exact for any input)
+    exact_case(f"scale {scale:+.3f}", "bhsd", 1, 2, 200, 277, 128, True, scale, seed=310,
+               integer=scale != 0.0)
+
+
+def test_e5m2_exact_shd_and_padded_v():
+    # [seq, heads, d] q/k; V key-major with rows of 400 keys for 333 live ones
+    exact_case("shd padded", "shd", 1, 4, 97, 333, 64, False, LN2, seed=311, pad_to=400)
+
+
+@pytest.mark.parametrize("sq,sk", [(1, 1), (5, 17), (64, 64), (300, 100), (100, 300)])
+def test_e5m2_exact_small_and_causal_shapes(sq, sk):
+    exact_case(f"sq{sq} sk{sk}", "bhsd", 1, 2, sq, sk, 64, True, LN2, seed=312 + sq)
+
+
+def test_e5m2_exact_eight_wave_workgroups():
+    # enough (batch, head) x 256-query tiles for the 8-wave launch
+    exact_case("8 waves", "bhsd", 1, 512, 600, 90, 64, True, LN2, seed=313)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_e5m2_gaussian_bound(causal, head_dim):
+    w = synth.custom(f"gauss d{head_dim}", "e5m2", "bhsd", 2, 2, 190, 421, head_dim,
+                     causal=causal, seed=320 + head_dim)
+    inp = synth.make_inputs(w)
+    say(f"[gpu] e5m2 bound {w.name} causal={causal}")
+    o, lse = run_e5m2(inp, causal, w.sm_scale)
+    o_ref, o_abs, vsum, lse_ref, delta = oracle_parts(inp, w.sm_scale, causal)
+    check_bound(w.name, o, lse, o_ref, o_abs, vsum, lse_ref, delta)
+
+
+def test_e5m2_long_causal_sampled():
+    """e5m2 [1,16,32768,128] causal with 1% of K rows x8: every output finite,
+    sampled rows within the rigorous bound of the oracle."""
+    w = synth.EXTRA_WORKLOADS["c5_e5m2"]
+    inp = synth.make_inputs(w)
+    say(f"[gpu] e5m2 sampled {w.name}")
+    o, lse = run_e5m2(inp, w.causal, w.sm_scale)
+    o_flat = o.reshape(-1, w.head_dim)
+    lse_flat = lse.reshape(-1)
+    rng = np.random.default_rng(6)
+    rows = sampled_rows(w, rng, 40)
+    bh_needed = sorted({int(r) // w.seq_q for r in rows})
+    heads = [(bh // w.heads, bh % w.heads) for bh in bh_needed]
+    q64 = inp.as_bhsd_f64("q", heads)
+    k64 = inp.as_bhsd_f64("k", heads)
+    v64 = inp.as_bhsd_f64("v", heads)
+    pos = {bh: n for n, bh in enumerate(bh_needed)}
+    local = np.array([pos[int(r) // w.seq_q] * w.seq_q + int(r) % w.seq_q for r in rows])
+    o_ref, lse_ref = oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=local)
+    o_abs, _ = oracle.forward_rows(q64, k64, np.abs(v64), w.sm_scale, w.causal, rows=local)
+    vsum = np.abs(v64).sum(axis=2)[:, 0]  # [n_heads, D]
+    vsum_rows = vsum[local // w.seq_q]
+    delta = np.array([score_delta(q64[r // w.seq_q, 0, r % w.seq_q][None], k64[r // w.seq_q, 0],
+                                  w.sm_scale, w.causal, np.array([r % w.seq_q]))[0]
+                      for r in local])
+    assert np.all(np.isfinite(o_flat)) and np.all(np.isfinite(lse_flat))
+    check_bound("c5 e5m2 rows", o_flat[rows], lse_flat[rows], o_ref, o_abs, vsum_rows, lse_ref,
+                delta)

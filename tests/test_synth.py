@@ -64,3 +64,33 @@ def test_stress_rows_are_scaled_exactly():
 def test_flop_convention():
     assert synth.WORKLOADS["c5"].flops() == 4.0 * 16 * 32768 * 32768 * 128 / 2
     assert synth.WORKLOADS["c2"].flops() == 4.0 * 16 * 1000 * 1537 * 64
+
+
+def test_e5m2_rounding_matches_torch_and_round_trips():
+    # RNE to e5m2 agrees with torch's float32 -> float8_e5m2 conversion over
+    # normals, subnormals, ties and the largest finite value
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(50000) * np.exp2(rng.uniform(-20, 15, 50000))
+    x = np.concatenate([x, [0.0, 2.0 ** -17, 3 * 2.0 ** -18, 2.0 ** -16, 1.125, 1.375, 2.5,
+                            -3.5 * 2.0 ** -16, 57344.0, -57344.0]])
+    x = x[np.abs(x) <= 57344.0].astype(np.float32).astype(np.float64)
+    mine = synth.round_to_dtype(x, "e5m2")
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    # every finite code decodes exactly and rounds back to itself (-0 aside)
+    codes = np.arange(256, dtype=np.uint8)
+    vals = synth.widen(codes, "e5m2")
+    fin = np.isfinite(vals) & (codes != 0x80)
+    assert np.array_equal(synth.round_to_dtype(vals[fin], "e5m2"), codes[fin])
+    assert vals[0x3C] == 1.0 and vals[0x7B] == 57344.0 and vals[0x01] == 2.0 ** -16
+
+
+def test_integer_score_inputs_give_small_integer_scores():
+    w = synth.custom("int scores", "e5m2", "bhsd", 1, 2, 40, 70, 64, seed=4)
+    inp = synth.make_integer_score_inputs(w)
+    q, k = inp.as_bhsd_f64("q"), inp.as_bhsd_f64("k")
+    assert np.all(np.count_nonzero(q, axis=-1) == 4)
+    s = q @ np.swapaxes(k, -1, -2)
+    assert np.array_equal(s, np.rint(s))
+    span = s.max(axis=-1) - s.min(axis=-1)
+    assert span.max() <= 16

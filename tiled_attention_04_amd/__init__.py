@@ -16,7 +16,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
 
-FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_E5M2 = 0, 1, 2, 3
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_LAYOUT", 6: "FA_ERR_HIP", 7: "FA_ERR_SCALE",
           8: "FA_ERR_WORKSPACE"}
@@ -113,7 +113,7 @@ def last_error():
 def _dtype_code(t):
     import torch
     codes = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
-             torch.bfloat16: FA_DTYPE_BF16}
+             torch.bfloat16: FA_DTYPE_BF16, torch.float8_e5m2: FA_DTYPE_E5M2}
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return codes[t.dtype]
@@ -136,12 +136,30 @@ def _dims(t, layout):
     return (B, H, S, D), FaStrides(sb, sh, ss, sd)
 
 
+def _dims_vt(vt, layout):
+    """Sizes and strides of a key-major V ([B, H, D, Sv], or [H, D, Sv] for "shd")."""
+    if layout == "shd":
+        H, D, S = vt.shape
+        sh, sd, ss = vt.stride()
+        B, sb = 1, 0
+    elif layout in ("bhsd", "bshd"):
+        B, H, D, S = vt.shape
+        sb, sh, sd, ss = vt.stride()
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    return (B, H, S, D), FaStrides(sb, sh, ss, sd)
+
+
 def forward(q, k, v, causal=False, sm_scale=None, layout="bhsd", out=None, lse=None,
             return_lse=True):
     """Attention forward on the current HIP stream.
 
     q: [B, H, Sq, D] ("bhsd"), [B, Sq, H, D] ("bshd") or [Sq, H, D] ("shd");
     k, v: the same with Sk.  sm_scale defaults to 1/sqrt(D).
+    For torch.float8_e5m2 inputs v is passed key-major instead: [B, H, D, Sv]
+    ([H, D, Sv] for "shd") with unit key stride and Sv >= Sk (keys past Sk
+    are padding and must be finite), e.g. ``v.transpose(-2, -1)`` of a
+    contiguous copy padded to a multiple of 16 keys.
     Returns (o, lse) with o like q and lse fp32 [B, H, Sq]; or o alone when
     return_lse is False (then lse is not computed unless passed in).
     """
@@ -150,8 +168,15 @@ def forward(q, k, v, causal=False, sm_scale=None, layout="bhsd", out=None, lse=N
         raise ValueError("q, k and v must be device tensors")
     (B, H, Sq, D), q_st = _dims(q, layout)
     (Bk, Hk, Sk, Dk), k_st = _dims(k, layout)
-    (Bv, Hv, Sv, Dv), v_st = _dims(v, layout)
-    if (Bk, Hk, Dk) != (B, H, D) or (Bv, Hv, Sv, Dv) != (B, H, Sk, D):
+    if q.dtype == torch.float8_e5m2:
+        (Bv, Hv, Sv, Dv), v_st = _dims_vt(v, layout)
+        if (Bv, Hv, Dv) != (B, H, D) or Sv < Sk:
+            raise ValueError("key-major v must be [B, H, D, Sv] with Sv >= Sk")
+    else:
+        (Bv, Hv, Sv, Dv), v_st = _dims(v, layout)
+        if (Bv, Hv, Sv, Dv) != (B, H, Sk, D):
+            raise ValueError("q, k, v shapes disagree")
+    if (Bk, Hk, Dk) != (B, H, D):
         raise ValueError("q, k, v shapes disagree")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share a dtype")

@@ -11,6 +11,7 @@
 #include "../../include/fa.h"
 #include "fa_fwd_kernels.hpp"
 #include "fa_bwd_kernels.hpp"
+#include "fa_fp8_kernels.hpp"
 
 namespace {
 
@@ -148,6 +149,27 @@ fa_status_t launch_combine(const fa::FwdArgs& a, void* stream) {
   return FA_OK;
 }
 
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_e5m2(fa::FwdArgs a) {
+  fa::fa_fwd_e5m2_body<D, NW>(a);
+}
+
+template <int NW>
+fa_status_t launch_e5m2_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
+  a.n_qtiles = (int32_t)((a.seq_q + 32 * NW - 1) / (32 * NW));
+  const int64_t grid = (int64_t)a.n_bh * a.n_qtiles;
+  if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
+  a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
+  if (head_dim <= 64) return launch(fa_fwd_e5m2<64, NW>, grid, 64 * NW, a, stream);
+  return launch(fa_fwd_e5m2<128, NW>, grid, 64 * NW, a, stream);
+}
+
+fa_status_t launch_e5m2(fa::FwdArgs& a, int64_t head_dim, void* stream) {
+  if (waves_16bit(a.n_bh, a.seq_q, head_dim) == 8) return launch_e5m2_nw<8>(a, head_dim, stream);
+  return launch_e5m2_nw<4>(a, head_dim, stream);
+}
+
 fa_status_t launch_f32(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   a.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
   const int64_t grid = (int64_t)a.n_bh * a.n_qtiles;
@@ -226,26 +248,41 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   if (seq_q > kInt32Max - 256 || seq_k > kInt32Max - 256 || batch > kInt32Max || heads > kInt32Max ||
       batch * heads > kInt32Max || batch * heads * seq_q > INT64_MAX / 2)
     return fail(FA_ERR_SHAPE, "a size exceeds the 32-bit index range");
-  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16 &&
+      dtype != FA_DTYPE_E5M2)
     return fail(FA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
   const bool f32 = dtype == FA_DTYPE_F32;
-  const int64_t hd_mult = f32 ? 4 : 8;
-  if (head_dim < 1 || head_dim > 256 || head_dim % hd_mult != 0)
-    return fail(FA_ERR_HEAD_DIM, "head_dim %lld must be in 1..256 and a multiple of %lld",
-                (long long)head_dim, (long long)hd_mult);
-  const int64_t mult = f32 ? 1 : 8;
-  fa_status_t s;
-  if ((s = check_strides("q", q_st, mult)) != FA_OK) return s;
-  if ((s = check_strides("k", k_st, mult)) != FA_OK) return s;
-  if ((s = check_strides("v", v_st, mult)) != FA_OK) return s;
-  if ((s = check_strides("o", o_st, mult)) != FA_OK) return s;
-  if (!std::isfinite(sm_scale)) return fail(FA_ERR_SCALE, "sm_scale must be finite");
+  const bool e5m2 = dtype == FA_DTYPE_E5M2;
   if (split_api) {
     if (splits < 0 || splits > fa::kMaxSplits)
       return fail(FA_ERR_WORKSPACE, "num_splits %d outside 0..%d", splits, fa::kMaxSplits);
-    if (splits == 0) splits = f32 ? 1 : choose_splits(batch * heads, seq_q, seq_k, head_dim, causal);
-    if (f32 && splits > 1) return fail(FA_ERR_DTYPE, "key splitting needs bf16 or fp16 inputs");
+    if (splits == 0)
+      splits = (f32 || e5m2) ? 1 : choose_splits(batch * heads, seq_q, seq_k, head_dim, causal);
+    if ((f32 || e5m2) && splits > 1)
+      return fail(FA_ERR_DTYPE, "key splitting needs bf16 or fp16 inputs");
   }
+  const int64_t hd_mult = f32 ? 4 : e5m2 ? 16 : 8;
+  const int64_t hd_max = e5m2 ? 128 : 256;
+  if (head_dim < 1 || head_dim > hd_max || head_dim % hd_mult != 0)
+    return fail(FA_ERR_HEAD_DIM, "head_dim %lld must be in 1..%lld and a multiple of %lld",
+                (long long)head_dim, (long long)hd_max, (long long)hd_mult);
+  const int64_t mult = f32 ? 1 : e5m2 ? 16 : 8;  // 16-byte rows
+  fa_status_t s;
+  if ((s = check_strides("q", q_st, mult)) != FA_OK) return s;
+  if ((s = check_strides("k", k_st, mult)) != FA_OK) return s;
+  if (e5m2) {
+    // V key-major: seq stride 1, one row of >= seq_k keys per dim
+    if (v_st.seq != 1) return fail(FA_ERR_LAYOUT, "v: e5m2 takes V key-major (seq stride 1)");
+    if (v_st.dim < seq_k || v_st.dim % 16 != 0 || v_st.dim >= kMaxSeqStride)
+      return fail(FA_ERR_LAYOUT, "v: dim stride %lld must be a multiple of 16, >= seq_k and < 2^24",
+                  (long long)v_st.dim);
+    if (v_st.batch < 0 || v_st.head < 0 || v_st.batch % 16 != 0 || v_st.head % 16 != 0)
+      return fail(FA_ERR_LAYOUT, "v: batch/head strides must be non-negative multiples of 16");
+  } else if ((s = check_strides("v", v_st, mult)) != FA_OK) {
+    return s;
+  }
+  if ((s = check_strides("o", o_st, mult)) != FA_OK) return s;
+  if (!std::isfinite(sm_scale)) return fail(FA_ERR_SCALE, "sm_scale must be finite");
   // an empty problem touches no memory, so its pointers may be NULL
   if (batch == 0 || heads == 0 || seq_q == 0) return FA_OK;
   if (!q || !k || !v || !o) return fail(FA_ERR_NULL, "q, k, v and o must be non-NULL");
@@ -276,6 +313,7 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   a.neg_scale = sm_scale < 0.f ? 1 : 0;
   a.causal = causal ? 1 : 0;
   a.n_splits = splits;
+  a.v_sd = v_st.dim;
   if (splits > 1) {
     a.part_o = (float*)workspace;
     a.part_lse = a.part_o + (size_t)splits * (size_t)(batch * heads) * (size_t)seq_q * (size_t)head_dim;
@@ -290,6 +328,7 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
       st = launch_16bit<_Float16>(a, head_dim, stream);
       if (st == FA_OK && splits > 1) st = launch_combine<_Float16>(a, stream);
       return st;
+    case FA_DTYPE_E5M2: return launch_e5m2(a, head_dim, stream);
     default: return launch_f32(a, head_dim, stream);
   }
 }
@@ -343,9 +382,11 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   if (seq_q > kInt32Max - 256 || seq_k > kInt32Max - 256 || batch > kInt32Max || heads > kInt32Max ||
       batch * heads > kInt32Max || batch * heads * seq_q > INT64_MAX / 2)
     return fail(FA_ERR_SHAPE, "a size exceeds the 32-bit index range");
-  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16 &&
+      dtype != FA_DTYPE_E5M2)
     return fail(FA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
-  if (dtype == FA_DTYPE_F32) return fail(FA_ERR_DTYPE, "the backward supports bf16 and fp16 only");
+  if (dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_E5M2)
+    return fail(FA_ERR_DTYPE, "the backward supports bf16 and fp16 only");
   if (head_dim < 1 || head_dim > 128 || head_dim % 8 != 0)
     return fail(FA_ERR_HEAD_DIM, "backward: head_dim %lld must be in 1..128 and a multiple of 8",
                 (long long)head_dim);
@@ -407,6 +448,6 @@ const char* fa_status_string(fa_status_t s) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"

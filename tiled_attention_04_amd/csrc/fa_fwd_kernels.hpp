@@ -71,6 +71,7 @@ struct FwdArgs {
   int64_t k_sb, k_sh, k_ss;
   int64_t v_sb, v_sh, v_ss;
   int64_t o_sb, o_sh, o_ss;
+  int64_t v_sd;      // dim stride of V (the e5m2 path takes V key-major: seq stride 1)
   int32_t heads, seq_q, seq_k, head_dim;
   int32_t n_qtiles;  // ceil(seq_q / BM)
   int32_t n_bh;      // batch * heads

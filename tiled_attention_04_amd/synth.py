@@ -16,14 +16,16 @@ given standard deviation -- "Understanding Triton Tutorials Part 2", section
     without replacement and those K rows are multiplied by ``factor`` (a power
     of two, so the scaling is exact).
 Storage: fp32 -> np.float32, fp16 -> np.float16, bf16 -> np.uint16 holding the
-bf16 bit pattern (NumPy has no bf16 type).
+bf16 bit pattern, e5m2 -> np.uint8 holding the float8 e5m2 bit pattern (OCP:
+sign, 5 exponent bits with bias 15, 2 mantissa bits -- the upper byte of an
+IEEE binary16; NumPy has neither type).
 """
 from dataclasses import dataclass, field
 import math
 
 import numpy as np
 
-DTYPES = ("fp32", "fp16", "bf16")
+DTYPES = ("fp32", "fp16", "bf16", "e5m2")
 LAYOUTS = ("shd", "bhsd")  # [seq, heads, d] (batch 1) or [batch, heads, seq, d]
 
 
@@ -87,6 +89,11 @@ EXTRA_WORKLOADS = {
                          "shd", 1, 12, 100, 4096, 64, 1.0, 0.5, False, seed=41),
     "short10": Workload("fp16 s_q=10 s_k=4096 h=12 d=64 seq-heads-d, non-causal", "fp16",
                         "shd", 1, 12, 10, 4096, 64, 1.0, 0.5, False, seed=42),
+    # the long causal workload with every input stored in float8 e5m2 (the
+    # fp8 variant of the tutorial's kernel): same draws, rounded to e5m2
+    "c5_e5m2": Workload("e5m2 [1,16,32768,128] causal, 1% of K rows x8", "e5m2", "bhsd", 1, 16,
+                        32768, 32768, 128, 1.0, 1.0 / math.sqrt(128.0), True, seed=25,
+                        stress_frac=0.01, stress_factor=8.0),
 }
 
 _CHUNK = 1 << 22
@@ -101,7 +108,28 @@ def round_to_dtype(x, dtype):
         return x.astype(np.float16)
     if dtype == "bf16":
         return _f64_to_bf16_bits(x)
+    if dtype == "e5m2":
+        return _f64_to_e5m2_bits(x)
     raise ValueError(dtype)
+
+
+E5M2_MAX = 57344.0  # 1.75 * 2^15
+
+
+def _f64_to_e5m2_bits(x):
+    """RNE to the e5m2 grid: 3 significant bits for |x| >= 2^-14, a fixed
+    quantum of 2^-16 below (subnormals); the rounded value is exact in
+    binary16, whose upper byte is the e5m2 code."""
+    if np.any(np.isnan(x)):
+        raise ValueError("NaN has no e5m2 code here")
+    a = np.abs(x)
+    _, ex = np.frexp(a)  # a = m 2^ex, 0.5 <= m < 1
+    quantum = np.where(a >= 2.0 ** -14, np.ldexp(1.0, ex - 3), 2.0 ** -16)
+    r = np.rint(a / quantum) * quantum  # np.rint: ties to even
+    if np.any(r > E5M2_MAX):
+        raise ValueError("value outside the e5m2 range")
+    h = np.copysign(r, x).astype(np.float16)  # exact
+    return (np.ascontiguousarray(h).view(np.uint16) >> np.uint16(8)).astype(np.uint8)
 
 
 def _f64_to_bf16_bits(x):
@@ -122,12 +150,16 @@ def widen(stored, dtype):
     if dtype == "bf16":
         u = np.asarray(stored, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(np.float64)
+    if dtype == "e5m2":
+        u = np.asarray(stored, dtype=np.uint8).astype(np.uint16) << np.uint16(8)
+        return u.view(np.float16).astype(np.float64)
     return np.asarray(stored).astype(np.float64)
 
 
 def _draw(rng, shape, std, dtype):
     n = int(np.prod(shape))
-    out_dtype = {"fp32": np.float32, "fp16": np.float16, "bf16": np.uint16}[dtype]
+    out_dtype = {"fp32": np.float32, "fp16": np.float16, "bf16": np.uint16,
+                 "e5m2": np.uint8}[dtype]
     out = np.empty(n, dtype=out_dtype)
     for s in range(0, n, _CHUNK):
         e = min(n, s + _CHUNK)
@@ -178,6 +210,25 @@ def make_inputs(w, seq_q=None, seq_k=None):
                 else:
                     k[b, h, idx, :] = scaled
     return Inputs(w, q, k, v, stressed)
+
+
+def make_integer_score_inputs(w, nonzeros=4):
+    """Inputs whose scores Q K^T are small integers: every Q row holds
+    ``nonzeros`` entries +-1 at distinct random dims (zeros elsewhere) and K
+    holds integers in [-2, 2]; V is drawn as in ``make_inputs``.  A row's
+    scores then span at most 4 * nonzeros, so with a scale of +-ln 2 every
+    softmax weight relative to the row maximum is an exact power of two no
+    smaller than 2^-16 (exact in every storage type here, e5m2 included)."""
+    rng = np.random.default_rng(w.seed)
+    qshape, kshape = w.shape("q"), w.shape("k")
+    rows = int(np.prod(qshape[:-1]))
+    q = np.zeros((rows, w.head_dim))
+    cols = np.argsort(rng.random((rows, w.head_dim)), axis=1)[:, :nonzeros]
+    signs = rng.choice([-1.0, 1.0], size=(rows, nonzeros))
+    np.put_along_axis(q, cols, signs, axis=1)
+    k = rng.integers(-2, 3, size=kshape).astype(np.float64)
+    v = _draw(rng, w.shape("v"), w.std, w.dtype)
+    return Inputs(w, round_to_dtype(q.reshape(qshape), w.dtype), round_to_dtype(k, w.dtype), v, {})
 
 
 def make_dout(w):
