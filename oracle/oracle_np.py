@@ -50,6 +50,60 @@ def attention_forward(q, k, v, sm_scale, causal, row_block=256):
     return o, lse
 
 
+def attention_forward_tiled(q, k, v, sm_scale, causal, block_m, block_n, lazy_threshold=0.0):
+    """The tiled online-softmax recurrence, in float64 -- the algorithm of
+    "[CS336] Assignment 2: Systems", section "FlashAttention V2: Forward Pass"
+    and of the inner loop of "Understanding Triton Tutorials Part 2",
+    section "Fused Attention 2", written out block by block: for each block of
+    ``block_m`` query rows, walk the key blocks of ``block_n`` keys keeping a
+    running maximum m, a running sum l and an unnormalised output O~; for a key
+    block with scores S (masked entries -inf)
+        m_new = max(m, rowmax S),  P = exp(S - m_new),
+        l = exp(m - m_new) l + rowsum P,  O~ = exp(m - m_new) O~ + P V,
+    then O = O~ / l and lse = m + log l.
+
+    ``lazy_threshold`` > 0 models the reading that m is only refreshed when the
+    block maximum exceeds it by more than the threshold (natural-log units);
+    any reference maximum gives the same O and lse in exact arithmetic.
+
+    Not used to produce expected values: it is pinned against the plain
+    definition (``attention_forward``) in the tests.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    o = np.empty((B, H, Sq, D), dtype=np.float64)
+    lse = np.empty((B, H, Sq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Sq, block_m):
+                rows = np.arange(r0, min(Sq, r0 + block_m))
+                m = np.full(rows.size, -np.inf)
+                l = np.zeros(rows.size)
+                acc = np.zeros((rows.size, D))
+                for c0 in range(0, Sk, block_n):
+                    cols = np.arange(c0, min(Sk, c0 + block_n))
+                    s = (q[b, h, rows] @ k[b, h, cols].T) * sm_scale
+                    if causal:
+                        s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+                    m_blk = s.max(axis=1)
+                    m_new = np.maximum(m, m_blk)
+                    if lazy_threshold > 0:
+                        m_new = np.where(m_blk > m + lazy_threshold, m_new, m)
+                    # rows with nothing visible so far keep m = -inf and add nothing
+                    ref = np.where(np.isfinite(m_new), m_new, 0.0)
+                    p = np.exp(s - ref[:, None])
+                    alpha = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
+                    l = alpha * l + p.sum(axis=1)
+                    acc = alpha[:, None] * acc + p @ v[b, h, cols]
+                    m = m_new
+                o[b, h, rows] = acc / l[:, None]
+                lse[b, h, rows] = m + np.log(l)
+    return o, lse
+
+
 def attention_backward(q, k, v, dout, sm_scale, causal):
     """Gradients dQ, dK, dV of O = attention(q, k, v) for upstream dout.
 
