@@ -61,56 +61,6 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-class SclkSampler:
-    """Samples the current shader clock level (MHz) from sysfs while the timed
-    region runs, if the box exposes it; reports None otherwise."""
-
-    def __init__(self, period_s=0.01):
-        import threading
-        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-        self.samples = []
-        self.period = period_s
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _read(self):
-        best = None
-        for p in self.paths:
-            try:
-                with open(p) as f:
-                    for line in f:
-                        if line.rstrip().endswith("*"):
-                            mhz = float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
-                            best = mhz if best is None else max(best, mhz)
-            except (OSError, ValueError, IndexError):
-                continue
-        return best
-
-    def _run(self):
-        while not self._stop.is_set():
-            v = self._read()
-            if v is not None:
-                self.samples.append(v)
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        if self.paths:
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self.paths:
-            self._thread.join()
-
-    def summary(self):
-        if not self.samples:
-            return None
-        return {"mean": round(sum(self.samples) / len(self.samples), 1),
-                "max": max(self.samples), "min": min(self.samples), "samples": len(self.samples),
-                "source": "pp_dpm_sclk (current level)"}
-
-
 def load_traffic():
     """HBM bytes per launch from the committed counter summary, if it matches
     the current kernel source; otherwise None."""
@@ -319,16 +269,15 @@ def main():
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    with SclkSampler() as sclk:
-        t_wall0 = time.perf_counter()
-        region0.record(stream)
-        for i in range(args.steps):
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-        region1.record(stream)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall0
+    t_wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
     ms_region = region0.elapsed_time(region1)
     per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     ms_avg = sum(per_launch) / len(per_launch)
@@ -373,7 +322,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms_avg": round(ms_avg, 5),
                      "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
-                     "kernel_ms_min": round(per_launch[0], 5), "sclk_mhz": sclk.summary()},
+                     "kernel_ms_min": round(per_launch[0], 5)},
         "context": {"rtx3090_unfused_per_call": CONTEXT_RTX3090},
     }
     if not args.no_cpu_baseline and args.workload == "c5":
