@@ -162,7 +162,7 @@ struct BwdQTile {
   static constexpr int KPER = (KINSTR + NW - 1) / NW, VPER = (VINSTR + NW - 1) / NW;
   static constexpr int KBYTES = BN * KR, VBYTES = BN * VR;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int LDS_BYTES = 2 * STAGE;  // two LDS objects of STAGE bytes
   static_assert(D % 16 == 0 && D <= 128, "head_dim padding");
   static_assert(KR >= DBLK * 64, "transposed reads of the K tile stay inside a row");
 };
@@ -174,8 +174,10 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
   typedef typename M::frag frag;
   constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK, KR = G::KR, VR = G::VR;
 
-  __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
-  FA_LDS char* lds = (FA_LDS char*)smem;
+  // the two tile stages as separate LDS objects, so that the compiler can
+  // tell reads of one stage from the asynchronous loads into the other
+  __shared__ __attribute__((aligned(1024))) char stage0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,12 +234,11 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
 #pragma unroll
   for (int n = 0; n < G::VPER; ++n)
     voff[n] = tile_slot_offset((wave + NW * n) * 64 + lane, BN, G::VSLOTS, a.v_ss, a.head_dim);
-  auto issue = [&](int j, int stage) {
+  auto issue = [&](int j, FA_LDS char* kb) {
     const int key0 = j * BN;
     const int rows = min(BN, a.seq_k - key0);
     const auto rk = make_rsrc(kg + (int64_t)key0 * a.k_ss, (rows - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2);
     const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
-    FA_LDS char* kb = lds + stage * G::STAGE;
     FA_LDS char* vb = kb + G::KBYTES;
 #pragma unroll
     for (int n = 0; n < G::KPER; ++n)
@@ -260,15 +261,9 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
   const int s16 = lane & 15;
   const int t_lane = (4 * hi + (s16 >> 2)) * KR + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
 
-  if (n_tiles > 0) {
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < n_tiles) issue(t + 1, stage ^ 1);
-    FA_LDS char* kb = lds + stage * G::STAGE;
+  // one key tile; its K / V are in stage kb, the next tile loads into nb
+  auto step = [&](int t, FA_LDS char* kb, FA_LDS char* nb) {
+    if (t + 1 < n_tiles) issue(t + 1, nb);
     FA_LDS char* vb = kb + G::KBYTES;
 
     // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks of the tile
@@ -324,6 +319,18 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
     __syncthreads();                // ... and everyone's; stage t is free
+  };
+
+  if (n_tiles > 0) {
+    issue(0, (FA_LDS char*)stage0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1);
+      step(t + 1, (FA_LDS char*)stage1, (FA_LDS char*)stage0);
+    }
+    if (t < n_tiles) step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1);
   }
 
   // dQ = scale * (K^T dS^T)^T, rounded to the input type
@@ -361,7 +368,12 @@ struct BwdKVTile {
   static constexpr int STAGE = 2 * TBYTES;       // Q tile + dO tile
   static constexpr int PROW = 64;                // scratch row: 32 keys x 2 bytes
   static constexpr int SCRATCH = 2 * BQ * PROW;  // P and dS of one wave
-  static constexpr int LDS_BYTES = 2 * STAGE + NW * SCRATCH;
+  // at d = 128 each wave keeps its 32 V rows in LDS rather than in KSTEPS
+  // registers (16 mod 256 byte rows: conflict-free 16-byte row reads)
+  static constexpr bool V_IN_LDS = (D == 128);
+  static constexpr int VR = D * 2 + 16;
+  static constexpr int VWBYTES = V_IN_LDS ? 32 * VR : 0;
+  static constexpr int LDS_BYTES = 2 * STAGE + NW * SCRATCH + NW * VWBYTES;  // over four objects
   static_assert(D % 16 == 0 && D <= 128, "head_dim padding");
   static_assert(QR >= DBLK * 64, "transposed reads stay inside a row");
 };
@@ -380,8 +392,14 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   typedef typename M::frag frag;
   constexpr int BQ = G::BQ, KSTEPS = G::KSTEPS, DBLK = G::DBLK, QR = G::QR;
 
-  __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
-  FA_LDS char* lds = (FA_LDS char*)smem;
+  // four LDS objects -- the two tile stages, the P/dS scratch and the V
+  // rows -- so that the compiler knows which accesses the asynchronous tile
+  // loads into one stage can touch, and does not make reads of the other
+  // stage or of the scratch wait for them
+  __shared__ __attribute__((aligned(1024))) char stage0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char scr_mem[NW * G::SCRATCH];
+  __shared__ __attribute__((aligned(1024))) char v_mem[G::V_IN_LDS ? NW * G::VWBYTES : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -408,7 +426,9 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   const int qt_end = (a.seq_q + BQ - 1) / BQ;
 
   // resident A operands: lane = (key l32, dims 8*hi..+7 of each k-step); K negated for scale < 0
-  frag kf[KSTEPS], vf[KSTEPS];
+  FA_LDS char* v_lds = (FA_LDS char*)v_mem + wave * G::VWBYTES;
+  const int v_lane = l32 * G::VR + hi * 16;
+  frag kf[KSTEPS], vf[G::V_IN_LDS ? 1 : KSTEPS];
   {
     const int32_t nk = wave_keys > 0 ? (wave_keys - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2 : 0;
     const int32_t nv = wave_keys > 0 ? (wave_keys - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2 : 0;
@@ -425,7 +445,10 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
           rv, in ? (uint32_t)(l32 * (int32_t)a.v_ss * 2 + col * 2) : kOutOfRange, 0, 0);
       rawk ^= (u32x4_t){sign, sign, sign, sign};
       kf[st] = __builtin_bit_cast(frag, rawk);
-      vf[st] = __builtin_bit_cast(frag, rawv);
+      if constexpr (G::V_IN_LDS)
+        *(FA_LDS u32x4_t*)(v_lds + v_lane + st * 32) = rawv;
+      else
+        vf[st] = __builtin_bit_cast(frag, rawv);
     }
   }
   const float c = a.c;
@@ -438,12 +461,11 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     qoff[n] = tile_slot_offset(slot, BQ, G::QSLOTS, a.q_ss, a.head_dim);
     doff[n] = tile_slot_offset(slot, BQ, G::QSLOTS, a.do_ss, a.head_dim);
   }
-  auto issue = [&](int j, int stage) {
+  auto issue = [&](int j, FA_LDS char* qb) {
     const int qa = j * BQ;
     const int rows = min(BQ, a.seq_q - qa);
     const auto rq = make_rsrc(qg + (int64_t)qa * a.q_ss, (rows - 1) * (int32_t)a.q_ss * 2 + a.head_dim * 2);
     const auto rd = make_rsrc(dog + (int64_t)qa * a.do_ss, (rows - 1) * (int32_t)a.do_ss * 2 + a.head_dim * 2);
-    FA_LDS char* qb = lds + stage * G::STAGE;
     FA_LDS char* db_ = qb + G::TBYTES;
 #pragma unroll
     for (int n = 0; n < G::QPER; ++n)
@@ -463,22 +485,24 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     dkacc[db] = (f32x16_t){};
   }
 
-  FA_LDS char* pscr = lds + 2 * G::STAGE + wave * G::SCRATCH;  // P, then dS at + BQ * PROW
+  FA_LDS char* pscr = (FA_LDS char*)scr_mem + wave * G::SCRATCH;  // P, then dS at + BQ * PROW
   const int q_lane = l32 * QR + hi * 16;                          // b128 row reads of Q / dO
   const int s16 = lane & 15;
   const int t_row = 4 * hi + (s16 >> 2);                          // transposing reads
   const int t_col = (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
   const int t_lane = t_row * QR + t_col;
 
-  if (qt0 < qt_end) {
-    issue(qt0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  for (int t = qt0; t < qt_end; ++t) {
-    const int stage = (t - qt0) & 1;
-    if (t + 1 < qt_end) issue(t + 1, stage ^ 1);
-    FA_LDS char* qb = lds + stage * G::STAGE;
+  // lse and delta of a query tile, loaded one tile ahead (index clamped, so
+  // the loads are unconditional)
+  auto row_stats = [&](int t, float& L, float& Dv) {
+    const int qi = min(t * BQ + l32, a.seq_q - 1);
+    L = lseg[qi];
+    Dv = delg[qi];
+  };
+  // one query tile; its Q / dO tile is in stage qb, the next tile loads
+  // into the other stage nb meanwhile
+  auto step = [&](int t, FA_LDS char* qb, FA_LDS char* nb, float L_cur, float D_cur) {
+    if (t + 1 < qt_end) issue(t + 1, nb);
     FA_LDS char* dob = qb + G::TBYTES;
 
     // S^T = K Q^T, dP^T = V dO^T: rows = this wave's 32 keys, column = query l32
@@ -488,14 +512,19 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
       const frag qfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + q_lane + st * 32));
       const frag dfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + q_lane + st * 32));
       s = M::mma(kf[st], qfr, s);
-      dp = M::mma(vf[st], dfr, dp);
+      if constexpr (G::V_IN_LDS) {
+        const frag vfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(v_lds + v_lane + st * 32));
+        dp = M::mma(vfr, dfr, dp);
+      } else {
+        dp = M::mma(vf[st], dfr, dp);
+      }
     }
 
     const int qa = t * BQ;
     const int my_q = qa + l32;
     const bool q_ok = my_q < a.seq_q;
-    const float L2 = q_ok ? lseg[my_q] * kLog2e : 0.f;
-    const float Dl = q_ok ? delg[my_q] : 0.f;
+    const float L2 = q_ok ? L_cur * kLog2e : 0.f;
+    const float Dl = q_ok ? D_cur : 0.f;
     const bool need_mask = !q_ok || (qa + BQ > a.seq_q) || (kw + 32 > a.seq_k) ||
                            (a.causal && kw + 31 > qa);
     // P and dS in the input type, written to the scratch in [query][key] order
@@ -558,6 +587,22 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
     __syncthreads();                // ... and everyone's; stage t is free
+  };
+
+  if (qt0 < qt_end) {
+    issue(qt0, (FA_LDS char*)stage0);
+    float L0, D0, L1 = 0.f, D1 = 0.f;
+    row_stats(qt0, L0, D0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int t = qt0;
+    for (; t + 1 < qt_end; t += 2) {
+      row_stats(t + 1, L1, D1);
+      step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1, L0, D0);
+      if (t + 2 < qt_end) row_stats(t + 2, L0, D0);
+      step(t + 1, (FA_LDS char*)stage1, (FA_LDS char*)stage0, L1, D1);
+    }
+    if (t < qt_end) step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1, L0, D0);
   }
 
   // dK = scale * dK^T^T, dV = dV^T^T, rounded to the input type
