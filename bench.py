@@ -111,11 +111,41 @@ def cpu_baseline(inp, target_s=15.0):
             break
         rate = row_flops(rows) / max(dt, 1e-3)  # oracle FLOP/s on this host
         n_rows = int(min(max_rows, max(2 * n_rows, rate * target_s / mean_row)))
-    return {"value": row_flops(rows) / dt / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{rows.size} evenly spaced query rows of the first {n_heads} (batch, head) "
-                      f"pairs of the same workload (fp64 C oracle, materialised softmax), "
-                      f"{dt:.1f} s wall"}
+    out = {"value": row_flops(rows) / dt / 1e12, "unit": "TFLOP/s",
+           "cores": oracle.max_threads(), "kind": "oracle",
+           "sample": f"{rows.size} evenly spaced query rows of the first {n_heads} (batch, head) "
+                     f"pairs of the same workload (fp64 C oracle, materialised softmax), "
+                     f"{dt:.1f} s wall"}
+    out["numpy_oracle"] = numpy_oracle_rate(inp)
+    return out
+
+
+def numpy_oracle_rate(inp, max_rows=8192):
+    """The NumPy float64 oracle (BLAS matmuls) on the first rows of one head:
+    with a causal mask, query rows 0..n-1 see only keys 0..n-1, so the
+    sample is exact with K and V cut to n keys."""
+    import numpy as np
+    from oracle import oracle_np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+    except ImportError:
+        threads = 0
+    w = inp.workload
+    n = min(w.seq_q, max_rows)
+    nk = n if w.causal else w.seq_k
+    q = inp.as_bhsd_f64("q", [(0, 0)])[:, :, :n]
+    k = inp.as_bhsd_f64("k", [(0, 0)])[:, :, :nk]
+    v = inp.as_bhsd_f64("v", [(0, 0)])[:, :, :nk]
+    t0 = time.perf_counter()
+    oracle_np.attention_forward(q, k, v, w.sm_scale, w.causal)
+    dt = time.perf_counter() - t0
+    i = np.arange(n)
+    keys = np.minimum(i + 1, nk) if w.causal else np.full(n, nk)
+    return {"value": float(np.sum(4.0 * keys * w.head_dim)) / dt / 1e12, "unit": "TFLOP/s",
+            "blas_threads": threads,
+            "sample": f"first {n} query rows of (batch 0, head 0), float64 NumPy oracle "
+                      f"(materialised softmax in row blocks), {dt:.1f} s wall"}
 
 
 def summarize_pmc(d):
