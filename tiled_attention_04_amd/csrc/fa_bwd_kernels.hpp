@@ -21,12 +21,14 @@
 //    dQ^T += K^T dS^T, whose K^T fragments come from LDS with transposing
 //    reads (ds_read_b64_tr_b16);
 //  * dK/dV kernel: 8 waves x 32 keys, each wave's K and V fragments
-//    resident in registers; Q and dO tiles of 32 queries stream through LDS.
-//    S^T and dP^T as above; P and dS (input type) go through a 4 KiB
-//    per-wave LDS scratch in [query][key] order and come back through
-//    transposing reads as key-major operands of dV^T += dO^T P and
-//    dK^T += Q^T dS, whose dO^T / Q^T fragments are transposing reads of the
-//    streamed tiles;
+//    resident (V in the wave's own LDS rows at head_dim 128); Q and dO
+//    tiles of 32 queries stream through LDS with the tile's lse and delta.
+//    S = Q K^T and dP = dO V^T (K, V as B operands), so lane l owns key
+//    l % 32 and register r holds query row 8 (r / 4) + 4 (l / 32) + r % 4 --
+//    the row order in which transposing reads deliver the k index of an A
+//    operand.  P and dS (input type) are therefore the B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS straight from registers, with the
+//    dO^T / Q^T fragments read transposed from the streamed tiles;
 //  * tiles read both row-wise (ds_read_b128) and transposed use a row stride
 //    s with s/16 odd and s, 2s, 3s (mod 256) at least 32 bytes from a
 //    multiple of 256, so neither access pattern has bank conflicts;
@@ -365,25 +367,19 @@ struct BwdKVTile {
   static constexpr int QINSTR = (BQ * QSLOTS + 63) / 64;  // wave-wide loads per tile
   static constexpr int QPER = (QINSTR + NW - 1) / NW;
   static constexpr int TBYTES = QINSTR * 1024;   // one tile, rounded to whole loads
-  static constexpr int STAGE = 2 * TBYTES;       // Q tile + dO tile
-  static constexpr int PROW = 64;                // scratch row: 32 keys x 2 bytes
-  static constexpr int SCRATCH = 2 * BQ * PROW;  // P and dS of one wave
+  static constexpr int LD_OFF = 2 * TBYTES;      // then the tile's lse*log2e and delta (fp32)
+  static constexpr int STAGE = 2 * TBYTES + 2 * BQ * 4;
   // at d = 128 each wave keeps its 32 V rows in LDS rather than in KSTEPS
   // registers (16 mod 256 byte rows: conflict-free 16-byte row reads)
   static constexpr bool V_IN_LDS = (D == 128);
   static constexpr int VR = D * 2 + 16;
   static constexpr int VWBYTES = V_IN_LDS ? 32 * VR : 0;
-  static constexpr int LDS_BYTES = 2 * STAGE + NW * SCRATCH + NW * VWBYTES;  // over four objects
+  static constexpr int LDS_BYTES = 2 * STAGE + NW * VWBYTES;  // over three objects
   static_assert(D % 16 == 0 && D <= 128, "head_dim padding");
   static_assert(QR >= DBLK * 64, "transposed reads stay inside a row");
 };
 
-// Byte offset of element (query row, key col) in a wave's P / dS scratch:
-// 64-byte rows, 16-byte chunks XOR-swizzled by (row / 4) % 4 so that the
-// row-wise writes of the 32 lanes spread over the banks.
-__device__ inline int scratch_off(int row, int col_bytes) {
-  return row * 64 + ((col_bytes & ~48) | (((col_bytes >> 4) ^ (row >> 2)) & 3) << 4);
-}
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T, int D, int NW>
 __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
@@ -392,13 +388,11 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   typedef typename M::frag frag;
   constexpr int BQ = G::BQ, KSTEPS = G::KSTEPS, DBLK = G::DBLK, QR = G::QR;
 
-  // four LDS objects -- the two tile stages, the P/dS scratch and the V
-  // rows -- so that the compiler knows which accesses the asynchronous tile
-  // loads into one stage can touch, and does not make reads of the other
-  // stage or of the scratch wait for them
+  // three LDS objects -- the two tile stages and the V rows -- so that the
+  // compiler knows which accesses the asynchronous tile loads into one stage
+  // can touch, and does not make reads of the other stage wait for them
   __shared__ __attribute__((aligned(1024))) char stage0[G::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) char scr_mem[NW * G::SCRATCH];
   __shared__ __attribute__((aligned(1024))) char v_mem[G::V_IN_LDS ? NW * G::VWBYTES : 16];
 
   const int tid = threadIdx.x;
@@ -425,7 +419,7 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   const int qt0 = a.causal ? min(k0, a.seq_q) / BQ : 0;
   const int qt_end = (a.seq_q + BQ - 1) / BQ;
 
-  // resident A operands: lane = (key l32, dims 8*hi..+7 of each k-step); K negated for scale < 0
+  // resident B operands: lane = (key l32, dims 8*hi..+7 of each k-step); K negated for scale < 0
   FA_LDS char* v_lds = (FA_LDS char*)v_mem + wave * G::VWBYTES;
   const int v_lane = l32 * G::VR + hi * 16;
   frag kf[KSTEPS], vf[G::V_IN_LDS ? 1 : KSTEPS];
@@ -485,90 +479,87 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     dkacc[db] = (f32x16_t){};
   }
 
-  FA_LDS char* pscr = (FA_LDS char*)scr_mem + wave * G::SCRATCH;  // P, then dS at + BQ * PROW
   const int q_lane = l32 * QR + hi * 16;                          // b128 row reads of Q / dO
   const int s16 = lane & 15;
   const int t_row = 4 * hi + (s16 >> 2);                          // transposing reads
   const int t_col = (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
   const int t_lane = t_row * QR + t_col;
 
-  // lse and delta of a query tile, loaded one tile ahead (index clamped, so
-  // the loads are unconditional)
-  auto row_stats = [&](int t, float& L, float& Dv) {
-    const int qi = min(t * BQ + l32, a.seq_q - 1);
-    L = lseg[qi];
-    Dv = delg[qi];
+  // lse * log2e and delta of query tile j: wave 0 loads them (lane = row,
+  // index clamped) while the tile before it is processed, and stores them
+  // next to the tile's Q and dO
+  float ld_l = 0.f, ld_d = 0.f;
+  auto stats_load = [&](int j) {
+    if (wave == 0) {
+      const int qi = min(j * BQ + l32, a.seq_q - 1);
+      ld_l = lseg[qi] * kLog2e;
+      ld_d = delg[qi];
+    }
   };
+  auto stats_store = [&](FA_LDS char* qb) {
+    if (wave == 0 && hi == 0) {
+      *(FA_LDS float*)(qb + G::LD_OFF + l32 * 4) = ld_l;
+      *(FA_LDS float*)(qb + G::LD_OFF + BQ * 4 + l32 * 4) = ld_d;
+    }
+  };
+
   // one query tile; its Q / dO tile is in stage qb, the next tile loads
   // into the other stage nb meanwhile
-  auto step = [&](int t, FA_LDS char* qb, FA_LDS char* nb, float L_cur, float D_cur) {
-    if (t + 1 < qt_end) issue(t + 1, nb);
+  auto step = [&](int t, FA_LDS char* qb, FA_LDS char* nb) {
+    if (t + 1 < qt_end) {
+      issue(t + 1, nb);
+      stats_load(t + 1);
+    }
     FA_LDS char* dob = qb + G::TBYTES;
 
-    // S^T = K Q^T, dP^T = V dO^T: rows = this wave's 32 keys, column = query l32
+    // S = Q K^T, dP = dO V^T: rows = the tile's 32 queries, column = key l32;
+    // register r of lane half hi holds query row 8 (r / 4) + 4 hi + r % 4,
+    // the row order of the transposing reads below, so P and dS serve as the
+    // B operands of the dV and dK products straight from registers
     f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       const frag qfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + q_lane + st * 32));
       const frag dfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + q_lane + st * 32));
-      s = M::mma(kf[st], qfr, s);
+      s = M::mma(qfr, kf[st], s);
       if constexpr (G::V_IN_LDS) {
         const frag vfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(v_lds + v_lane + st * 32));
-        dp = M::mma(vfr, dfr, dp);
+        dp = M::mma(dfr, vfr, dp);
       } else {
-        dp = M::mma(vf[st], dfr, dp);
+        dp = M::mma(dfr, vf[st], dp);
       }
     }
 
     const int qa = t * BQ;
-    const int my_q = qa + l32;
-    const bool q_ok = my_q < a.seq_q;
-    const float L2 = q_ok ? L_cur * kLog2e : 0.f;
-    const float Dl = q_ok ? D_cur : 0.f;
-    const bool need_mask = !q_ok || (qa + BQ > a.seq_q) || (kw + 32 > a.seq_k) ||
-                           (a.causal && kw + 31 > qa);
-    // P and dS in the input type, written to the scratch in [query][key] order
+    const int my_k = kw + l32;
+    const bool need_mask = (qa + BQ > a.seq_q) || (kw + 32 > a.seq_k) || (a.causal && kw + 31 > qa);
+    // P = exp2(s c - L2) and dS = P (dP - D) in the input type, paired along queries
     uint32_t pp[8], ps[8];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p0 = fast_exp2(__builtin_fmaf(s[r], c, -L2));
-      float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -L2));
-      if (need_mask) {
-        const int kk = kw + 8 * (r >> 2) + 4 * hi + (r & 3);
-        p0 = (q_ok && kk < a.seq_k && (!a.causal || kk <= my_q)) ? p0 : 0.f;
-        p1 = (q_ok && kk + 1 < a.seq_k && (!a.causal || kk + 1 <= my_q)) ? p1 : 0.f;
-      }
-      pp[r >> 1] = M::pack2(p0, p1);
-      ps[r >> 1] = M::pack2(p0 * (dp[r] - Dl), p1 * (dp[r + 1] - Dl));
-    }
-#pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int off = scratch_off(l32, (8 * j + 4 * hi) * 2);
-      *(FA_LDS u32x2_t*)(pscr + off) = (u32x2_t){pp[2 * j], pp[2 * j + 1]};
-      *(FA_LDS u32x2_t*)(pscr + BQ * G::PROW + off) = (u32x2_t){ps[2 * j], ps[2 * j + 1]};
+      const int row = 8 * j + 4 * hi;
+      const f32x4_t L4 = *(FA_LDS f32x4_t*)(qb + G::LD_OFF + row * 4);
+      const f32x4_t D4 = *(FA_LDS f32x4_t*)(qb + G::LD_OFF + BQ * 4 + row * 4);
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int r = 4 * j + i;
+        float p0 = fast_exp2(__builtin_fmaf(s[r], c, -L4[i]));
+        float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -L4[i + 1]));
+        if (need_mask) {
+          const int q = qa + row + i;
+          p0 = (q < a.seq_q && my_k < a.seq_k && (!a.causal || my_k <= q)) ? p0 : 0.f;
+          p1 = (q + 1 < a.seq_q && my_k < a.seq_k && (!a.causal || my_k <= q + 1)) ? p1 : 0.f;
+        }
+        pp[r >> 1] = M::pack2(p0, p1);
+        ps[r >> 1] = M::pack2(p0 * (dp[r] - D4[i]), p1 * (dp[r + 1] - D4[i + 1]));
+      }
     }
 
     // dV^T += dO^T P and dK^T += Q^T dS: two 16-query steps per 32-dim block
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      frag pfr, sfr;
-      {
-        const int r0 = 16 * u + t_row;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (FA_LDS i16x4_t*)(pscr + scratch_off(r0, t_col)));
-        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (FA_LDS i16x4_t*)(pscr + scratch_off(r0 + 8, t_col)));
-        const i16x4_t lo2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (FA_LDS i16x4_t*)(pscr + BQ * G::PROW + scratch_off(r0, t_col)));
-        const i16x4_t up2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (FA_LDS i16x4_t*)(pscr + BQ * G::PROW + scratch_off(r0 + 8, t_col)));
-        const u32x4_t praw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                              __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
-        const u32x4_t sraw = {__builtin_bit_cast(u32x2_t, lo2)[0], __builtin_bit_cast(u32x2_t, lo2)[1],
-                              __builtin_bit_cast(u32x2_t, up2)[0], __builtin_bit_cast(u32x2_t, up2)[1]};
-        pfr = __builtin_bit_cast(frag, praw);
-        sfr = __builtin_bit_cast(frag, sraw);
-      }
+      const frag pfr = __builtin_bit_cast(frag, (u32x4_t){pp[4 * u], pp[4 * u + 1], pp[4 * u + 2], pp[4 * u + 3]});
+      const frag sfr = __builtin_bit_cast(frag, (u32x4_t){ps[4 * u], ps[4 * u + 1], ps[4 * u + 2], ps[4 * u + 3]});
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         FA_LDS char* d0 = dob + t_lane + (16 * u) * QR + db * 64;
@@ -585,24 +576,23 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
         dkacc[db] = M::mma(__builtin_bit_cast(frag, qraw), sfr, dkacc[db]);
       }
     }
+    if (t + 1 < qt_end) stats_store(nb);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
     __syncthreads();                // ... and everyone's; stage t is free
   };
 
   if (qt0 < qt_end) {
     issue(qt0, (FA_LDS char*)stage0);
-    float L0, D0, L1 = 0.f, D1 = 0.f;
-    row_stats(qt0, L0, D0);
+    stats_load(qt0);
+    stats_store((FA_LDS char*)stage0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int t = qt0;
     for (; t + 1 < qt_end; t += 2) {
-      row_stats(t + 1, L1, D1);
-      step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1, L0, D0);
-      if (t + 2 < qt_end) row_stats(t + 2, L0, D0);
-      step(t + 1, (FA_LDS char*)stage1, (FA_LDS char*)stage0, L1, D1);
+      step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1);
+      step(t + 1, (FA_LDS char*)stage1, (FA_LDS char*)stage0);
     }
-    if (t < qt_end) step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1, L0, D0);
+    if (t < qt_end) step(t, (FA_LDS char*)stage0, (FA_LDS char*)stage1);
   }
 
   // dK = scale * dK^T^T, dV = dV^T^T, rounded to the input type
