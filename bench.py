@@ -233,8 +233,8 @@ def main():
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              "supported (heads shard across GPUs with no exchange; see the design notes)",
+        print(f"bench.py: the benchmark runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (heads would shard across GPUs with no exchange)",
               file=sys.stderr)
         return 2
 
