@@ -178,10 +178,12 @@ size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int6
  *   delta    fp32 [batch, heads, seq_q] contiguous, caller-owned; written
  *            with D (the call's working vector, readable afterwards)
  *   dq, dk, dv  outputs, shaped like q, k, v, via dq_st/dk_st/dv_st
- * All tensors share `dtype`, which must be FA_DTYPE_F16 or FA_DTYPE_BF16;
- * head_dim must be a multiple of 8 in 1..128.  Accumulation is fp32; P and
- * dS are rounded to the input type before their products, and the
- * gradients are rounded to nearest-even into the input type.  Same
+ * All tensors share `dtype`: FA_DTYPE_F16 or FA_DTYPE_BF16 (head_dim a
+ * multiple of 8 in 1..128), or FA_DTYPE_F32 (head_dim a multiple of 4 in
+ * 1..128; a small-problem path on the fp32 MFMA).  Accumulation is fp32; for
+ * 16-bit inputs P and dS are rounded to the input type before their
+ * products, and the gradients are rounded to nearest-even into the input
+ * type; fp32 inputs keep P and dS in fp32.  Same
  * visibility rule (causal, top-left) and sm_scale as fa_fwd; lse must come
  * from fa_fwd (or equal it) for the same q, k, sm_scale and causal.  Keys
  * that no query sees get zero dk and dv (also when seq_q == 0).
@@ -190,11 +192,12 @@ size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int6
  * synchronisation).  No output may overlap an input.
  *
  * Validation on the host before any HIP call: the fa_fwd rules for sizes,
- * strides and sm_scale over all eight tensors; dtype FA_DTYPE_F32 or
- * FA_DTYPE_E5M2 -> FA_ERR_DTYPE; head_dim > 128 -> FA_ERR_HEAD_DIM; batch or heads == 0
+ * strides and sm_scale over all eight tensors; dtype FA_DTYPE_E5M2 ->
+ * FA_ERR_DTYPE; head_dim > 128 -> FA_ERR_HEAD_DIM; batch or heads == 0
  * -> FA_OK with nothing launched; k, v, dk, dv NULL, or (seq_q > 0) q, o,
- * dout, lse, delta, dq NULL -> FA_ERR_NULL; a tensor not 16-byte aligned or
- * lse/delta not 4-byte aligned -> FA_ERR_LAYOUT.  If a launch fails
+ * dout, lse, delta, dq NULL -> FA_ERR_NULL; a tensor not 16-byte aligned
+ * (16-bit) or 4-byte aligned (fp32), or lse/delta not 4-byte aligned ->
+ * FA_ERR_LAYOUT.  If a launch fails
  * (FA_ERR_HIP) the launches before it in this call stay enqueued.
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

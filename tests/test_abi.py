@@ -109,7 +109,8 @@ def call_bwd(q=P, k=P, v=P, o=P, do=P, lse=P, delta=P, dq=P, dk=P, dv=P, batch=1
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(batch=-1), 2), (dict(sq=-2), 2), (dict(sk=0), 2), (dict(sq=1 << 31), 2),
-    (dict(dtype=F32), 3), (dict(dtype=E5M2), 3), (dict(dtype=5), 3),
+    (dict(dtype=E5M2), 3), (dict(dtype=5), 3), (dict(dtype=F32, d=6), 4),
+    (dict(dtype=F32, d=132), 4), (dict(dtype=F32, dq=P + 2), 5), (dict(dtype=F32, k=None), 1),
     (dict(d=0), 4), (dict(d=136), 4), (dict(d=256), 4), (dict(d=60), 4),
     (dict(sts={"do": S(0, 0, 64, 2)}), 5), (dict(sts={"dk": S(0, -64, 64, 1)}), 5),
     (dict(sts={"dv": S(0, 0, 68, 1)}), 5), (dict(sts={"o": S(0, 0, 1 << 24, 1)}), 5),
@@ -124,6 +125,13 @@ def test_bwd_validation_errors(kwargs, code):
     rc = call_bwd(**kwargs)
     assert rc == code, (kwargs, rc, fa.last_error())
     assert fa.last_error() != ""
+
+
+def test_bwd_fp32_accepts_unaligned_strides():
+    # fp32 rows need only 4-byte alignment: a seq stride of 65 passes, and
+    # the call then stops at the NULL q
+    rc = call_bwd(q=None, sts={"q": S(0, 0, 65, 1), "dq": S(0, 0, 65, 1)}, dtype=F32)
+    assert rc == 1, fa.last_error()
 
 
 def test_bwd_empty_problem_is_ok_without_pointers():

@@ -197,6 +197,19 @@ void fa_bwd_dkv(fa::BwdArgs a) {
   fa::fa_bwd_dkv_body<T, D, 8>(a);
 }
 
+// fp32 backward (one wave per SIMD: the fp32 fragments take twice the registers)
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dq_f32(fa::BwdArgs a) {
+  fa::fa_bwd_dq_f32_body<D>(a);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkv_f32(fa::BwdArgs a) {
+  fa::fa_bwd_dkv_f32_body<D>(a);
+}
+
 template <typename Kernel>
 fa_status_t launch_bwd(Kernel kernel, int64_t grid, int threads, const fa::BwdArgs& args,
                        void* stream) {
@@ -223,6 +236,28 @@ fa_status_t launch_bwd_dp(fa::BwdArgs a, void* stream) {
   }
   a.n_tiles = (int32_t)((a.seq_k + 255) / 256);
   return launch_bwd(fa_bwd_dkv<T, DP>, (int64_t)a.n_bh * a.n_tiles, 512, a, stream);
+}
+
+// fp32: D, then dQ (query blocks of 128), then dK/dV (key blocks of 128)
+template <int D>
+fa_status_t launch_bwd_f32_d(fa::BwdArgs a, void* stream) {
+  fa_status_t s;
+  const int64_t rows = (int64_t)a.n_bh * a.seq_q;
+  if (rows > 0) {
+    if ((s = launch_bwd(fa::fa_bwd_delta<float>, (rows + 31) / 32, 256, a, stream)) != FA_OK) return s;
+    a.n_tiles = (int32_t)((a.seq_q + 127) / 128);
+    if ((s = launch_bwd(fa_bwd_dq_f32<D>, (int64_t)a.n_bh * a.n_tiles, 256, a, stream)) != FA_OK)
+      return s;
+  }
+  a.n_tiles = (int32_t)((a.seq_k + 127) / 128);
+  return launch_bwd(fa_bwd_dkv_f32<D>, (int64_t)a.n_bh * a.n_tiles, 256, a, stream);
+}
+
+fa_status_t launch_bwd_f32(const fa::BwdArgs& a, int64_t head_dim, void* stream) {
+  if (head_dim <= 32) return launch_bwd_f32_d<32>(a, stream);
+  if (head_dim <= 64) return launch_bwd_f32_d<64>(a, stream);
+  if (head_dim <= 96) return launch_bwd_f32_d<96>(a, stream);
+  return launch_bwd_f32_d<128>(a, stream);
 }
 
 template <typename T>
@@ -385,24 +420,28 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16 &&
       dtype != FA_DTYPE_E5M2)
     return fail(FA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
-  if (dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_E5M2)
-    return fail(FA_ERR_DTYPE, "the backward supports bf16 and fp16 only");
-  if (head_dim < 1 || head_dim > 128 || head_dim % 8 != 0)
-    return fail(FA_ERR_HEAD_DIM, "backward: head_dim %lld must be in 1..128 and a multiple of 8",
-                (long long)head_dim);
+  if (dtype == FA_DTYPE_E5M2)
+    return fail(FA_ERR_DTYPE, "the backward supports fp32, bf16 and fp16");
+  const bool f32 = dtype == FA_DTYPE_F32;
+  const int64_t hd_mult = f32 ? 4 : 8;
+  if (head_dim < 1 || head_dim > 128 || head_dim % hd_mult != 0)
+    return fail(FA_ERR_HEAD_DIM, "backward: head_dim %lld must be in 1..128 and a multiple of %lld",
+                (long long)head_dim, (long long)hd_mult);
   fa_status_t s;
   const fa_strides_t* sts[8] = {&q_st, &k_st, &v_st, &o_st, &do_st, &dq_st, &dk_st, &dv_st};
   const char* names[8] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
   for (int i = 0; i < 8; ++i)
-    if ((s = check_strides(names[i], *sts[i], 8)) != FA_OK) return s;
+    if ((s = check_strides(names[i], *sts[i], f32 ? 1 : 8)) != FA_OK) return s;
   if (!std::isfinite(sm_scale)) return fail(FA_ERR_SCALE, "sm_scale must be finite");
   if (batch == 0 || heads == 0) return FA_OK;  // nothing to read or write
   if (!k || !v || !dk || !dv) return fail(FA_ERR_NULL, "k, v, dk and dv must be non-NULL");
   if (seq_q > 0 && (!q || !o || !dout || !lse || !delta || !dq))
     return fail(FA_ERR_NULL, "q, o, dout, lse, delta and dq must be non-NULL");
-  const void* p16[8] = {q, k, v, o, dout, dq, dk, dv};
+  const void* ptrs[8] = {q, k, v, o, dout, dq, dk, dv};
+  const uintptr_t align = f32 ? 4 : 16;
   for (int i = 0; i < 8; ++i)
-    if (p16[i] && !aligned(p16[i], 16)) return fail(FA_ERR_LAYOUT, "%s must be 16-byte aligned", names[i]);
+    if (ptrs[i] && !aligned(ptrs[i], align))
+      return fail(FA_ERR_LAYOUT, "%s must be %d-byte aligned", names[i], (int)align);
   if ((lse && !aligned(lse, 4)) || (delta && !aligned(delta, 4)))
     return fail(FA_ERR_LAYOUT, "lse and delta must be 4-byte aligned");
 
@@ -427,6 +466,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   a.neg_scale = sm_scale < 0.f ? 1 : 0;
   a.causal = causal ? 1 : 0;
   a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
+  if (f32) return launch_bwd_f32(a, head_dim, stream);
   if (dtype == FA_DTYPE_BF16) return launch_bwd_16bit<__bf16>(a, head_dim, stream);
   return launch_bwd_16bit<_Float16>(a, head_dim, stream);
 }

@@ -119,15 +119,21 @@ __global__ __launch_bounds__(256) void fa_bwd_delta(BwdArgs a) {
     const T* orow = (const T*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)i * a.o_ss;
     const T* drow =
         (const T*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)i * a.do_ss;
+    if constexpr (sizeof(T) == 4) {
+      // fp32 rows are only 4-byte aligned: element loads
+      for (int d = sub * 16; d < min(a.head_dim, sub * 16 + 16); ++d)
+        part = __builtin_fmaf((float)drow[d], (float)orow[d], part);
+    } else {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int d0 = sub * 16 + half * 8;
-      if (d0 < a.head_dim) {
-        typedef T t8 __attribute__((ext_vector_type(8)));
-        const t8 ov = *(const t8*)(orow + d0);
-        const t8 dv = *(const t8*)(drow + d0);
+      for (int half = 0; half < 2; ++half) {
+        const int d0 = sub * 16 + half * 8;
+        if (d0 < a.head_dim) {
+          typedef T t8 __attribute__((ext_vector_type(8)));
+          const t8 ov = *(const t8*)(orow + d0);
+          const t8 dv = *(const t8*)(drow + d0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)dv[e], (float)ov[e], part);
+          for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)dv[e], (float)ov[e], part);
+        }
       }
     }
   }
@@ -614,6 +620,216 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
                           M::pack2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3])};
       __builtin_amdgcn_raw_buffer_store_b64(wk, rdk, ok ? krow + d0 * 2 : kOutOfRange, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b64(wv, rdv, ok ? vrow + d0 * 2 : kOutOfRange, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: a small-problem path in the style of the fp32 forward -- the
+// same two phases with v_mfma_f32_32x32x2f32, single-buffered LDS tiles
+// filled with plain loads, P and dS kept in fp32.  D = head_dim rounded up to
+// 32.  An MFMA of this shape contracts 2 elements: lane half hi supplies
+// k-slot hi, and every operand below addresses its element by the same
+// (register, hi) -> key or query map, so each product sees matching k.
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdF32 {
+  static constexpr int NW = 4;
+  static constexpr int KSTEPS = D / 2;
+  static constexpr int DBLK = D / 32;
+  static constexpr int ROW = D + 1;  // floats; odd stride spreads rows over banks
+  static_assert(D % 32 == 0 && D <= 128, "head_dim padding");
+};
+
+__device__ inline f32x16_t mma_f32(float a, float b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// dQ: 4 waves x 32 queries; 64-key K/V tiles.  S^T = K Q^T, dP^T = V dO^T
+// (lane = query), dQ^T += K^T dS^T.
+template <int D>
+__device__ __forceinline__ void fa_bwd_dq_f32_body(const BwdArgs& a) {
+  using G = BwdF32<D>;
+  constexpr int BN = 64, NW = G::NW, KSTEPS = G::KSTEPS, DBLK = G::DBLK, ROW = G::ROW;
+  __shared__ float kt_lds[BN * ROW];
+  __shared__ float vt_lds[BN * ROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  int bh, qt;
+  map_bwd_workgroup(a, blockIdx.x, a.causal != 0, bh, qt);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const float* qg = (const float*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const float* dog = (const float*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh;
+  const float* kg = (const float*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const float* vg = (const float*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  float* dqg = (float*)a.dq + (int64_t)b * a.dq_sb + (int64_t)h * a.dq_sh;
+
+  const int q0 = qt * 32 * NW;
+  const int qw = q0 + wave * 32, my_q = qw + l32;
+  const bool q_ok = my_q < a.seq_q;
+  const int wave_last = min(qw + 31, a.seq_q - 1);
+  const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + 32 * NW)) : a.seq_k;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  float qf[KSTEPS], dof[KSTEPS];
+  const float qsign = a.neg_scale ? -1.f : 1.f;
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st) {
+    const int col = 2 * st + hi;
+    const bool in = q_ok && col < a.head_dim;
+    qf[st] = in ? qsign * qg[(int64_t)my_q * a.q_ss + col] : 0.f;
+    dof[st] = in ? dog[(int64_t)my_q * a.do_ss + col] : 0.f;
+  }
+  const float L2 = q_ok ? a.lse[(int64_t)bh * a.seq_q + my_q] * kLog2e : 0.f;
+  const float Dl = q_ok ? a.delta[(int64_t)bh * a.seq_q + my_q] : 0.f;
+  const float c = a.c;
+
+  f32x16_t acc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) acc[db] = (f32x16_t){};
+
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();  // previous tile consumed
+    const int key0 = t * BN;
+    for (int e = tid; e < BN * D; e += 64 * NW) {
+      const int row = e / D, col = e - (e / D) * D;
+      const bool ok = key0 + row < a.seq_k && col < a.head_dim;
+      kt_lds[row * ROW + col] = ok ? kg[(int64_t)(key0 + row) * a.k_ss + col] : 0.f;
+      vt_lds[row * ROW + col] = ok ? vg[(int64_t)(key0 + row) * a.v_ss + col] : 0.f;
+    }
+    __syncthreads();
+    if (qw >= a.seq_q || (a.causal && key0 > wave_last)) continue;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st) {
+        s = mma_f32(kt_lds[(kb2 * 32 + l32) * ROW + 2 * st + hi], qf[st], s);
+        dp = mma_f32(vt_lds[(kb2 * 32 + l32) * ROW + 2 * st + hi], dof[st], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);  // key of register r
+        const int key = key0 + kl;
+        const bool vis = q_ok && key < a.seq_k && (!a.causal || key <= my_q);
+        const float p = vis ? fast_exp2(__builtin_fmaf(s[r], c, -L2)) : 0.f;
+        const float ds = p * (dp[r] - Dl);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+          acc[db] = mma_f32(kt_lds[kl * ROW + db * 32 + l32], ds, acc[db]);
+      }
+    }
+  }
+  if (!q_ok) return;
+  const float sc = a.scale;
+  float* row = dqg + (int64_t)my_q * a.dq_ss;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = db * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (d < a.head_dim) row[d] = acc[db][r] * sc;
+    }
+}
+
+// dK/dV: 4 waves x 32 keys; 32-query Q/dO tiles with their lse and delta.
+// S = Q K^T, dP = dO V^T (rows = queries, lane = key), then
+// dV^T += dO^T P and dK^T += Q^T dS.
+template <int D>
+__device__ __forceinline__ void fa_bwd_dkv_f32_body(const BwdArgs& a) {
+  using G = BwdF32<D>;
+  constexpr int BQ = 32, NW = G::NW, KSTEPS = G::KSTEPS, DBLK = G::DBLK, ROW = G::ROW;
+  __shared__ float q_lds[BQ * ROW];
+  __shared__ float do_lds[BQ * ROW];
+  __shared__ float l_lds[BQ];
+  __shared__ float d_lds[BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  int bh, kt;
+  map_bwd_workgroup(a, blockIdx.x, false, bh, kt);
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const float* qg = (const float*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const float* dog = (const float*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh;
+  const float* kg = (const float*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
+  const float* vg = (const float*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  float* dkg = (float*)a.dk + (int64_t)b * a.dk_sb + (int64_t)h * a.dk_sh;
+  float* dvg = (float*)a.dv + (int64_t)b * a.dv_sb + (int64_t)h * a.dv_sh;
+  const float* lseg = a.lse + (int64_t)bh * a.seq_q;
+  const float* delg = a.delta + (int64_t)bh * a.seq_q;
+
+  const int k0 = kt * 32 * NW;
+  const int kw = k0 + wave * 32, my_k = kw + l32;
+  const bool k_ok = my_k < a.seq_k;
+  const int qt0 = a.causal ? min(k0, a.seq_q) / BQ : 0;
+  const int qt_end = (a.seq_q + BQ - 1) / BQ;
+
+  float kf[KSTEPS], vf[KSTEPS];
+  const float ksign = a.neg_scale ? -1.f : 1.f;
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st) {
+    const int col = 2 * st + hi;
+    const bool in = k_ok && col < a.head_dim;
+    kf[st] = in ? ksign * kg[(int64_t)my_k * a.k_ss + col] : 0.f;
+    vf[st] = in ? vg[(int64_t)my_k * a.v_ss + col] : 0.f;
+  }
+  const float c = a.c;
+  f32x16_t dvacc[DBLK], dkacc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) {
+    dvacc[db] = (f32x16_t){};
+    dkacc[db] = (f32x16_t){};
+  }
+
+  for (int t = qt0; t < qt_end; ++t) {
+    __syncthreads();  // previous tile consumed
+    const int qa = t * BQ;
+    for (int e = tid; e < BQ * D; e += 64 * NW) {
+      const int row = e / D, col = e - (e / D) * D;
+      const bool ok = qa + row < a.seq_q && col < a.head_dim;
+      q_lds[row * ROW + col] = ok ? qg[(int64_t)(qa + row) * a.q_ss + col] : 0.f;
+      do_lds[row * ROW + col] = ok ? dog[(int64_t)(qa + row) * a.do_ss + col] : 0.f;
+    }
+    if (tid < BQ) {
+      const bool ok = qa + tid < a.seq_q;
+      l_lds[tid] = ok ? lseg[qa + tid] * kLog2e : 0.f;
+      d_lds[tid] = ok ? delg[qa + tid] : 0.f;
+    }
+    __syncthreads();
+    if (kw >= a.seq_k || (a.causal && kw > qa + BQ - 1)) continue;
+    f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      s = mma_f32(q_lds[l32 * ROW + 2 * st + hi], kf[st], s);
+      dp = mma_f32(do_lds[l32 * ROW + 2 * st + hi], vf[st], dp);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ql = 8 * (r >> 2) + 4 * hi + (r & 3);  // query of register r
+      const int q = qa + ql;
+      const bool vis = k_ok && q < a.seq_q && (!a.causal || my_k <= q);
+      const float p = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l_lds[ql])) : 0.f;
+      const float ds = p * (dp[r] - d_lds[ql]);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        dvacc[db] = mma_f32(do_lds[ql * ROW + db * 32 + l32], p, dvacc[db]);
+        dkacc[db] = mma_f32(q_lds[ql * ROW + db * 32 + l32], ds, dkacc[db]);
+      }
+    }
+  }
+  if (!k_ok) return;
+  const float sc = a.scale;
+  float* krow = dkg + (int64_t)my_k * a.dk_ss;
+  float* vrow = dvg + (int64_t)my_k * a.dv_ss;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d = db * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (d < a.head_dim) {
+        krow[d] = dkacc[db][r] * sc;
+        vrow[d] = dvacc[db][r];
+      }
     }
 }
 
