@@ -104,6 +104,58 @@ def attention_forward_tiled(q, k, v, sm_scale, causal, block_m, block_n, lazy_th
     return o, lse
 
 
+def attention_backward_tiled(q, k, v, dout, sm_scale, causal, block_m, block_n):
+    """The two-phase tiled backward, in float64 -- the blocked form of
+    "[CS336] Assignment 2: Systems", section "FlashAttention V2: Backward
+    Pass", split as that page's Triton version splits it: with O and L from
+    the plain forward (``attention_forward``) and D = rowsum(dO o O),
+      phase 1, per block of ``block_m`` queries, over the key blocks:
+        P = exp(S - L) (masked entries 0), dP = dO V^T, dS = P o (dP - D),
+        dQ += scale dS K;
+      phase 2, per block of ``block_n`` keys, over the query blocks:
+        the same P and dS, dV += P^T dO, dK += scale dS^T Q.
+    Each phase recomputes P.  Not used to produce expected values: it is
+    pinned against ``attention_backward`` in the tests.  Returns (dq, dk, dv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    o, lse = attention_forward(q, k, v, sm_scale, causal)
+    delta = np.sum(dout * o, axis=-1)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+
+    def blocks(b, h, rows, cols):
+        s = (q[b, h, rows] @ k[b, h, cols].T) * sm_scale
+        p = np.exp(s - lse[b, h, rows][:, None])
+        if causal:
+            p = np.where(cols[None, :] > rows[:, None], 0.0, p)
+        dp = dout[b, h, rows] @ v[b, h, cols].T
+        ds = p * (dp - delta[b, h, rows][:, None])
+        return p, ds
+
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Sq, block_m):  # phase 1: dQ
+                rows = np.arange(r0, min(Sq, r0 + block_m))
+                for c0 in range(0, Sk, block_n):
+                    cols = np.arange(c0, min(Sk, c0 + block_n))
+                    _, ds = blocks(b, h, rows, cols)
+                    dq[b, h, rows] += sm_scale * (ds @ k[b, h, cols])
+            for c0 in range(0, Sk, block_n):  # phase 2: dK, dV
+                cols = np.arange(c0, min(Sk, c0 + block_n))
+                for r0 in range(0, Sq, block_m):
+                    rows = np.arange(r0, min(Sq, r0 + block_m))
+                    p, ds = blocks(b, h, rows, cols)
+                    dv[b, h, cols] += p.T @ dout[b, h, rows]
+                    dk[b, h, cols] += sm_scale * (ds.T @ q[b, h, rows])
+    return dq, dk, dv
+
+
 def attention_backward(q, k, v, dout, sm_scale, causal):
     """Gradients dQ, dK, dV of O = attention(q, k, v) for upstream dout.
 

@@ -62,3 +62,17 @@ def test_lazy_refresh_is_exercised():
         o, lse = oracle_np.attention_forward_tiled(q, k, v, 1.0, False, 1, 16, lazy_threshold=thr)
         assert np.max(np.abs(o - o_ref)) <= 1e-12
         assert abs(lse[0, 0, 0] - lse_ref[0, 0, 0]) <= 1e-12
+
+
+@pytest.mark.parametrize("block_m,block_n", [(1, 1), (3, 5), (16, 64), (128, 32)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_phase_backward_matches_definition(block_m, block_n, causal):
+    # the kernels' backward split (dQ per query block, dK/dV per key block,
+    # P recomputed from L in both) against the materialised gradients
+    q, k, v = _inputs(4, 1, 2, 70, 93, 12, big_rows=3)
+    dout = np.random.default_rng(5).standard_normal(q.shape)
+    scale = -0.4 if causal else 0.3
+    ref = oracle_np.attention_backward(q, k, v, dout, scale, causal)
+    got = oracle_np.attention_backward_tiled(q, k, v, dout, scale, causal, block_m, block_n)
+    for g, r in zip(got, ref[:3]):
+        assert np.max(np.abs(g - r)) <= 1e-12 * max(1.0, np.max(np.abs(r)))
