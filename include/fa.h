@@ -68,7 +68,7 @@ typedef struct {
  *
  * FA_DTYPE_E5M2 (the fp8 path of "Understanding Triton Tutorials Part 2",
  * section "Fused Attention 2": all of q, k, v, o in float8 e5m2, v stored
- * transposed): head_dim a multiple of 16 up to 128; v is passed key-major --
+ * transposed): head_dim a multiple of 16 up to 256; v is passed key-major --
  * v_st.seq == 1 and v_st.dim, the distance between the key rows of two
  * dims, a multiple of 16 and >= seq_k; other strides multiples of 16.  Keys
  * between seq_k and the next multiple of 16 are read from the row (their P
@@ -96,10 +96,11 @@ typedef struct {
  *   that would exceed int32                      -> FA_ERR_SHAPE
  *   dtype unknown                                -> FA_ERR_DTYPE
  *   head_dim < 1, > 256, or not a multiple of 8 (f16/bf16) or 4 (f32);
- *   e5m2: > 128 or not a multiple of 16            -> FA_ERR_HEAD_DIM
+ *   e5m2: not a multiple of 16                     -> FA_ERR_HEAD_DIM
  *   a dim stride != 1, any negative stride, a seq stride >= 2^24 elements,
  *   a batch/head/seq stride not a multiple of 8 elements (f16/bf16) or of
- *   16 (e5m2); e5m2 v not key-major as above     -> FA_ERR_LAYOUT
+ *   16 (e5m2); e5m2 v not key-major as above, or (head_dim - 1) * v's dim
+ *   stride + 64 beyond 2^31 - 1                  -> FA_ERR_LAYOUT
  *   sm_scale NaN or infinite                     -> FA_ERR_SCALE
  *   batch, heads or seq_q == 0                   -> FA_OK, nothing launched
  *                                                   (pointers may be NULL)

@@ -81,7 +81,8 @@ def test_fp32_accepts_unaligned_strides():
 
 
 @pytest.mark.parametrize("kwargs,code", [
-    (dict(d=136), 4), (dict(d=256), 4), (dict(d=24), 4), (dict(d=8), 4),
+    (dict(d=264), 4), (dict(d=24), 4), (dict(d=8), 4), (dict(d=200), 4),
+    (dict(d=256, vs=S(0, 0, 1, (1 << 24) - 16)), 5),
     (dict(vs=CONTIG), 5), (dict(vs=S(0, 0, 1, 112)), 5), (dict(vs=S(0, 0, 1, 136)), 5),
     (dict(vs=S(8, 0, 1, 128)), 5), (dict(vs=S(0, 0, 1, 1 << 24)), 5),
     (dict(qs=S(0, 0, 72, 1)), 5), (dict(ks=S(0, 8, 64, 1)), 5), (dict(q=P + 8), 5),

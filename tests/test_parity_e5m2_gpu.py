@@ -161,7 +161,7 @@ def exact_case(name, layout, B, H, Sq, Sk, D, causal, scale, seed, pad_to=None, 
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("head_dim", [16, 48, 64, 80, 128])
+@pytest.mark.parametrize("head_dim", [16, 48, 64, 80, 128, 192, 256])
 def test_e5m2_exact_ragged(causal, head_dim):
     # several 64-key tiles, a key count that is no multiple of 16, a query
     # count that is no multiple of 32
@@ -192,7 +192,7 @@ def test_e5m2_exact_eight_wave_workgroups():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
 def test_e5m2_gaussian_bound(causal, head_dim):
     w = synth.custom(f"gauss d{head_dim}", "e5m2", "bhsd", 2, 2, 190, 421, head_dim,
                      causal=causal, seed=320 + head_dim)

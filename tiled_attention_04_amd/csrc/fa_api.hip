@@ -155,6 +155,12 @@ void fa_fwd_e5m2(fa::FwdArgs a) {
   fa::fa_fwd_e5m2_body<D, NW>(a);
 }
 
+// head_dim 129..256: one wave per SIMD (the O^T accumulator alone takes 128 VGPRs)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_fwd_e5m2_d256(fa::FwdArgs a) {
+  fa::fa_fwd_e5m2_body<256, 4>(a);
+}
+
 template <int NW>
 fa_status_t launch_e5m2_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   a.n_qtiles = (int32_t)((a.seq_q + 32 * NW - 1) / (32 * NW));
@@ -166,6 +172,13 @@ fa_status_t launch_e5m2_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
 }
 
 fa_status_t launch_e5m2(fa::FwdArgs& a, int64_t head_dim, void* stream) {
+  if (head_dim > 128) {
+    a.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
+    const int64_t grid = (int64_t)a.n_bh * a.n_qtiles;
+    if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
+    a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
+    return launch(fa_fwd_e5m2_d256, grid, 256, a, stream);
+  }
   if (waves_16bit(a.n_bh, a.seq_q, head_dim) == 8) return launch_e5m2_nw<8>(a, head_dim, stream);
   return launch_e5m2_nw<4>(a, head_dim, stream);
 }
@@ -297,7 +310,7 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
       return fail(FA_ERR_DTYPE, "key splitting needs bf16 or fp16 inputs");
   }
   const int64_t hd_mult = f32 ? 4 : e5m2 ? 16 : 8;
-  const int64_t hd_max = e5m2 ? 128 : 256;
+  const int64_t hd_max = 256;
   if (head_dim < 1 || head_dim > hd_max || head_dim % hd_mult != 0)
     return fail(FA_ERR_HEAD_DIM, "head_dim %lld must be in 1..%lld and a multiple of %lld",
                 (long long)head_dim, (long long)hd_max, (long long)hd_mult);
@@ -311,6 +324,9 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     if (v_st.dim < seq_k || v_st.dim % 16 != 0 || v_st.dim >= kMaxSeqStride)
       return fail(FA_ERR_LAYOUT, "v: dim stride %lld must be a multiple of 16, >= seq_k and < 2^24",
                   (long long)v_st.dim);
+    // a V tile is addressed by 32-bit byte offsets spanning head_dim key rows
+    if ((head_dim - 1) * v_st.dim + 64 > kInt32Max)
+      return fail(FA_ERR_LAYOUT, "v: (head_dim - 1) * dim stride exceeds the 32-bit tile range");
     if (v_st.batch < 0 || v_st.head < 0 || v_st.batch % 16 != 0 || v_st.head % 16 != 0)
       return fail(FA_ERR_LAYOUT, "v: batch/head strides must be non-negative multiples of 16");
   } else if ((s = check_strides("v", v_st, mult)) != FA_OK) {

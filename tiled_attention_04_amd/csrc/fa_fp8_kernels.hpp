@@ -53,7 +53,7 @@ struct TileF8 {
   static constexpr int VBYTES = VINSTR * 1024;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;
-  static_assert(D == 64 || D == 128, "fp8 head_dim padding");
+  static_assert(D == 64 || D == 128 || D == 256, "fp8 head_dim padding");
   static_assert((BN * KSLOTS) % 64 == 0, "whole wave loads of K");
 };
 
