@@ -180,8 +180,9 @@ size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int6
  *            with D (the call's working vector, readable afterwards)
  *   dq, dk, dv  outputs, shaped like q, k, v, via dq_st/dk_st/dv_st
  * All tensors share `dtype`: FA_DTYPE_F16 or FA_DTYPE_BF16 (head_dim a
- * multiple of 8 in 1..128), or FA_DTYPE_F32 (head_dim a multiple of 4 in
- * 1..128; a small-problem path on the fp32 MFMA).  Accumulation is fp32; for
+ * multiple of 8 in 1..256; above 128 one wave per SIMD), or FA_DTYPE_F32
+ * (head_dim a multiple of 4 in 1..128; a small-problem path on the fp32
+ * MFMA).  Accumulation is fp32; for
  * 16-bit inputs P and dS are rounded to the input type before their
  * products, and the gradients are rounded to nearest-even into the input
  * type; fp32 inputs keep P and dS in fp32.  Same
@@ -194,7 +195,7 @@ size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int6
  *
  * Validation on the host before any HIP call: the fa_fwd rules for sizes,
  * strides and sm_scale over all eight tensors; dtype FA_DTYPE_E5M2 ->
- * FA_ERR_DTYPE; head_dim > 128 -> FA_ERR_HEAD_DIM; batch or heads == 0
+ * FA_ERR_DTYPE; head_dim outside the ranges above -> FA_ERR_HEAD_DIM; batch or heads == 0
  * -> FA_OK with nothing launched; k, v, dk, dv NULL, or (seq_q > 0) q, o,
  * dout, lse, delta, dq NULL -> FA_ERR_NULL; a tensor not 16-byte aligned
  * (16-bit) or 4-byte aligned (fp32), or lse/delta not 4-byte aligned ->

@@ -112,7 +112,7 @@ def call_bwd(q=P, k=P, v=P, o=P, do=P, lse=P, delta=P, dq=P, dk=P, dv=P, batch=1
     (dict(batch=-1), 2), (dict(sq=-2), 2), (dict(sk=0), 2), (dict(sq=1 << 31), 2),
     (dict(dtype=E5M2), 3), (dict(dtype=5), 3), (dict(dtype=F32, d=6), 4),
     (dict(dtype=F32, d=132), 4), (dict(dtype=F32, dq=P + 2), 5), (dict(dtype=F32, k=None), 1),
-    (dict(d=0), 4), (dict(d=136), 4), (dict(d=256), 4), (dict(d=60), 4),
+    (dict(d=0), 4), (dict(d=264), 4), (dict(d=260), 4), (dict(d=60), 4),
     (dict(sts={"do": S(0, 0, 64, 2)}), 5), (dict(sts={"dk": S(0, -64, 64, 1)}), 5),
     (dict(sts={"dv": S(0, 0, 68, 1)}), 5), (dict(sts={"o": S(0, 0, 1 << 24, 1)}), 5),
     (dict(dq=P + 8), 5), (dict(do=P + 4), 5), (dict(lse=P + 2), 5), (dict(delta=P + 1), 5),

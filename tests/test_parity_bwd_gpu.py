@@ -91,7 +91,7 @@ def full_bwd_parity(w, causal=None, sm_scale=None, tag=""):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("head_dim", [32, 64, 80, 96, 128])
+@pytest.mark.parametrize("head_dim", [32, 64, 80, 96, 128, 200, 256])
 def test_bwd_ragged(dtype, causal, head_dim):
     w = synth.custom(f"bwd {dtype} d{head_dim}", dtype, "bhsd", 2, 3, 129, 200, head_dim,
                      causal=causal, seed=100 + head_dim)

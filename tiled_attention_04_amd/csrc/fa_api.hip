@@ -210,6 +210,20 @@ void fa_bwd_dkv(fa::BwdArgs a) {
   fa::fa_bwd_dkv_body<T, D, 8>(a);
 }
 
+// head_dim 129..256: one wave per SIMD (the dK/dV accumulators alone take 256 VGPRs);
+// dK/dV workgroups of 4 waves (128 keys), so two tile stages and the V rows fit in LDS
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dq_d256(fa::BwdArgs a) {
+  fa::fa_bwd_dq_body<T, 256, 4>(a);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkv_d256(fa::BwdArgs a) {
+  fa::fa_bwd_dkv_body<T, 256, 4>(a);
+}
+
 // fp32 backward (one wave per SIMD: the fp32 fragments take twice the registers)
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -274,7 +288,22 @@ fa_status_t launch_bwd_f32(const fa::BwdArgs& a, int64_t head_dim, void* stream)
 }
 
 template <typename T>
+fa_status_t launch_bwd_16bit_d256(fa::BwdArgs a, void* stream) {
+  fa_status_t s;
+  const int64_t rows = (int64_t)a.n_bh * a.seq_q;
+  if (rows > 0) {
+    if ((s = launch_bwd(fa::fa_bwd_delta<T>, (rows + 31) / 32, 256, a, stream)) != FA_OK) return s;
+    a.n_tiles = (int32_t)((a.seq_q + 127) / 128);
+    if ((s = launch_bwd(fa_bwd_dq_d256<T>, (int64_t)a.n_bh * a.n_tiles, 256, a, stream)) != FA_OK)
+      return s;
+  }
+  a.n_tiles = (int32_t)((a.seq_k + 127) / 128);
+  return launch_bwd(fa_bwd_dkv_d256<T>, (int64_t)a.n_bh * a.n_tiles, 256, a, stream);
+}
+
+template <typename T>
 fa_status_t launch_bwd_16bit(const fa::BwdArgs& a, int64_t head_dim, void* stream) {
+  if (head_dim > 128) return launch_bwd_16bit_d256<T>(a, stream);
   if (head_dim <= 32) return launch_bwd_dp<T, 32>(a, stream);
   if (head_dim <= 64) return launch_bwd_dp<T, 64>(a, stream);
   if (head_dim <= 80) return launch_bwd_dp<T, 80>(a, stream);
@@ -440,9 +469,10 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
     return fail(FA_ERR_DTYPE, "the backward supports fp32, bf16 and fp16");
   const bool f32 = dtype == FA_DTYPE_F32;
   const int64_t hd_mult = f32 ? 4 : 8;
-  if (head_dim < 1 || head_dim > 128 || head_dim % hd_mult != 0)
-    return fail(FA_ERR_HEAD_DIM, "backward: head_dim %lld must be in 1..128 and a multiple of %lld",
-                (long long)head_dim, (long long)hd_mult);
+  const int64_t hd_max = f32 ? 128 : 256;
+  if (head_dim < 1 || head_dim > hd_max || head_dim % hd_mult != 0)
+    return fail(FA_ERR_HEAD_DIM, "backward: head_dim %lld must be in 1..%lld and a multiple of %lld",
+                (long long)head_dim, (long long)hd_max, (long long)hd_mult);
   fa_status_t s;
   const fa_strides_t* sts[8] = {&q_st, &k_st, &v_st, &o_st, &do_st, &dq_st, &dk_st, &dv_st};
   const char* names[8] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};

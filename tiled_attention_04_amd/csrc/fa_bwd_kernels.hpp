@@ -104,7 +104,7 @@ constexpr int dual_stride(int min_bytes) {
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_t dO_it O_it  (fp32), 8 lanes per row, 16 dims per lane.
+// D_i = sum_t dO_it O_it  (fp32), 8 lanes per row.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void fa_bwd_delta(BwdArgs a) {
@@ -120,20 +120,17 @@ __global__ __launch_bounds__(256) void fa_bwd_delta(BwdArgs a) {
     const T* drow =
         (const T*)a.dout + (int64_t)b * a.do_sb + (int64_t)h * a.do_sh + (int64_t)i * a.do_ss;
     if constexpr (sizeof(T) == 4) {
-      // fp32 rows are only 4-byte aligned: element loads
-      for (int d = sub * 16; d < min(a.head_dim, sub * 16 + 16); ++d)
+      // fp32 rows are only 4-byte aligned: element loads, lane sub takes dims sub + 8 i
+      for (int d = sub; d < a.head_dim; d += 8)
         part = __builtin_fmaf((float)drow[d], (float)orow[d], part);
     } else {
+      // 8-element chunks: lane sub takes chunks sub, sub + 8, ... (dims 8 sub + 64 i ..)
+      for (int d0 = 8 * sub; d0 < a.head_dim; d0 += 64) {
+        typedef T t8 __attribute__((ext_vector_type(8)));
+        const t8 ov = *(const t8*)(orow + d0);
+        const t8 dv = *(const t8*)(drow + d0);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int d0 = sub * 16 + half * 8;
-        if (d0 < a.head_dim) {
-          typedef T t8 __attribute__((ext_vector_type(8)));
-          const t8 ov = *(const t8*)(orow + d0);
-          const t8 dv = *(const t8*)(drow + d0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)dv[e], (float)ov[e], part);
-        }
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)dv[e], (float)ov[e], part);
       }
     }
   }
@@ -171,7 +168,7 @@ struct BwdQTile {
   static constexpr int KBYTES = BN * KR, VBYTES = BN * VR;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;  // two LDS objects of STAGE bytes
-  static_assert(D % 16 == 0 && D <= 128, "head_dim padding");
+  static_assert(D % 16 == 0 && D <= 256, "head_dim padding");
   static_assert(KR >= DBLK * 64, "transposed reads of the K tile stay inside a row");
 };
 
@@ -377,11 +374,11 @@ struct BwdKVTile {
   static constexpr int STAGE = 2 * TBYTES + 2 * BQ * 4;
   // at d = 128 each wave keeps its 32 V rows in LDS rather than in KSTEPS
   // registers (16 mod 256 byte rows: conflict-free 16-byte row reads)
-  static constexpr bool V_IN_LDS = (D == 128);
+  static constexpr bool V_IN_LDS = (D >= 128);
   static constexpr int VR = D * 2 + 16;
   static constexpr int VWBYTES = V_IN_LDS ? 32 * VR : 0;
   static constexpr int LDS_BYTES = 2 * STAGE + NW * VWBYTES;  // over three objects
-  static_assert(D % 16 == 0 && D <= 128, "head_dim padding");
+  static_assert(D % 16 == 0 && D <= 256, "head_dim padding");
   static_assert(QR >= DBLK * 64, "transposed reads stay inside a row");
 };
 
