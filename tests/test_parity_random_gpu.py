@@ -36,7 +36,7 @@ def draw_case(seed, backward=False):
     seq_q = int(rng.choice([1, int(rng.integers(2, 80)), int(rng.integers(80, 400))]))
     seq_k = int(rng.choice([1, int(rng.integers(2, 80)), int(rng.integers(80, 500))]))
     step = 4 if dtype == "fp32" else 8
-    d_max = 128 if backward else 256
+    d_max = 128 if (backward and dtype == "fp32") else 256
     head_dim = int(rng.integers(1, d_max // step + 1)) * step
     causal = bool(rng.integers(0, 2))
     scale = float(rng.choice([-1.0, 1.0]) * rng.uniform(0.05, 1.5) / math.sqrt(head_dim))
