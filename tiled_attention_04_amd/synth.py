@@ -167,6 +167,26 @@ def _draw(rng, shape, std, dtype):
     return out.reshape(shape)
 
 
+def device_normal(shape, dtype, seed, std=1.0, device="cuda"):
+    """Seeded N(0, std^2) values drawn on the device by torch's generator and
+    rounded to ``dtype`` (torch's own round-to-nearest-even conversion), for
+    inputs too large to draw on the host.  Both sides of a comparison read the
+    same tensor: the GPU path directly, the oracle through host copies of the
+    slices it checks."""
+    import torch
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16,
+           "e5m2": torch.float8_e5m2}[dtype]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=tdt, device=device)
+    flat = out.view(-1)
+    step = 1 << 28  # draw in fp32 chunks of 1 GiB
+    for s in range(0, flat.numel(), step):
+        e = min(flat.numel(), s + step)
+        flat[s:e] = (torch.randn(e - s, generator=gen, device=device) * std).to(tdt)
+    return out
+
+
 @dataclass
 class Inputs:
     workload: Workload
