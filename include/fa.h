@@ -87,9 +87,11 @@ typedef struct {
  *
  * Ownership: every pointer is caller-owned device memory.  The library does
  * not allocate, free or synchronise; it only launches kernels on `stream`
- * (a hipStream_t; NULL means the default stream).  A fault in the kernel
- * surfaces at the caller's next synchronisation.  o must not overlap q, k, v
- * or lse (undefined, not checked).
+ * (a hipStream_t; NULL means the default stream), with no memset, copy or
+ * event, so a call may be recorded into a HIP graph under stream capture and
+ * replayed (the buffers are those of the recorded call).  A fault in the
+ * kernel surfaces at the caller's next synchronisation.  o must not overlap
+ * q, k, v or lse (undefined, not checked).
  *
  * Validation happens on the host before any HIP call, in this order:
  *   batch, heads, seq_q < 0, seq_k < 1, or any size, the grid or an index
