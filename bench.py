@@ -216,8 +216,8 @@ def bench_bwd(args, w, inp, up, q, k, v, o, lse, layout, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c5",
                     choices=["c2", "c3", "c4", "c5", "short100", "short10", "c5_e5m2"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
