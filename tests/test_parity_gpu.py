@@ -98,6 +98,15 @@ def test_heads_seq_dim_layout_distinct_head_strides():
     full_parity(synth.make_inputs(w2), name="hsd fp16 q_ctx=10")
 
 
+def test_issue_matrix_800_heads():
+    """q_ctx = 10 against 4096 keys with 800 heads, d = 32, [seq, heads, d]: the
+    largest head count of the issue's test matrix (a grid of 800 one-wave-deep
+    query tiles)."""
+    w = synth.custom("issue h800", "fp16", "shd", 1, 800, 10, 4096, 32, std=0.5, sm_scale=0.5,
+                     seed=510)
+    full_parity(synth.make_inputs(w), name="shd fp16 q_ctx=10 heads=800")
+
+
 def test_strided_views():
     """Inputs that are views with padded rows and a permuted layout."""
     import torch
