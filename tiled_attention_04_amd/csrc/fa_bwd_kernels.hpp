@@ -87,21 +87,16 @@ __device__ inline void map_bwd_workgroup(const BwdArgs& a, int wg, bool reverse,
   tile = reverse ? a.n_tiles - 1 - rank : rank;
 }
 
-// Smallest row stride (bytes, multiple of 16, >= min_bytes) that is free of
-// bank conflicts both for 16 lanes reading 16 consecutive rows at one 16-byte
-// chunk and for 16 lanes reading 4 consecutive rows x 32 bytes.
-constexpr int dual_stride(int min_bytes) {
-  int st = (min_bytes + 15) / 16 * 16;
-  for (;; st += 16) {
-    const int s = st % 256;
-    bool ok = ((s / 16) % 2) == 1;
-    for (int m = 1; m <= 3; ++m) {
-      const int r = (m * s) % 256;
-      ok = ok && r >= 32 && r <= 224;
-    }
-    if (ok) return st;
-  }
-}
+// Rows of the tiles that are read both row-wise (16-byte MFMA operand reads,
+// 16 lanes = 16 consecutive rows at one 16-byte chunk per LDS cycle) and
+// transposed (ds_read_b64_tr_b16, 32 lanes = 4 consecutive rows x 64 bytes per
+// cycle).  The row stride is 64 or 192 mod 256 bytes, which puts the 4 rows of
+// a transposing read into the four 64-byte bank windows; inside each 64-byte
+// group the four 16-byte chunks of row r are stored XOR-permuted by
+// (r / 4) % 4, so the 16 rows of a row-wise read, which share each window four
+// at a time, use its four different 16-byte slots.  Slot p of row r holds
+// chunk swz_chunk(p, r) of the row (and chunk p sits in that same slot).
+__device__ constexpr int swz_chunk(int p, int row) { return (p & ~3) | ((p & 3) ^ ((row >> 2) & 3)); }
 
 // ---------------------------------------------------------------------------
 // D_i = sum_t dO_it O_it  (fp32), 8 lanes per row.
@@ -151,6 +146,17 @@ __device__ inline uint32_t tile_slot_offset(int slot, int rows, int slots, int64
                                            : kOutOfRange;
 }
 
+// The same for the swizzled dual-read tiles: slot p < data_slots of a row
+// receives chunk swz_chunk(p, row); the padding slots read nothing.
+__device__ inline uint32_t swz_slot_offset(int slot, int rows, int slots, int data_slots,
+                                           int64_t seq_stride, int head_dim) {
+  const int row = slot / slots, p = slot - (slot / slots) * slots;
+  const int ch = swz_chunk(p, row);
+  return (row < rows && p < data_slots && ch * 8 < head_dim)
+             ? (uint32_t)(row * (int32_t)seq_stride * 2 + ch * 16)
+             : kOutOfRange;
+}
+
 // ---------------------------------------------------------------------------
 // dQ kernel: one workgroup per (batch*head, block of 32*NW queries).
 // ---------------------------------------------------------------------------
@@ -160,7 +166,7 @@ struct BwdQTile {
   static constexpr int BN = 64;                  // keys per K/V tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = (D + 31) / 32;
-  static constexpr int KR = dual_stride(D * 2);  // K rows: b128 + transposed
+  static constexpr int KR = tr_row_stride(DBLK * 64);  // K rows: b128 + transposed, swizzled
   static constexpr int VR = D * 2 + 16;          // V rows: b128 only (16 mod 256)
   static constexpr int KSLOTS = KR / 16, VSLOTS = VR / 16;
   static constexpr int KINSTR = BN * KSLOTS / 64, VINSTR = BN * VSLOTS / 64;
@@ -235,7 +241,8 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
   uint32_t koff[G::KPER], voff[G::VPER];
 #pragma unroll
   for (int n = 0; n < G::KPER; ++n)
-    koff[n] = tile_slot_offset((wave + NW * n) * 64 + lane, BN, G::KSLOTS, a.k_ss, a.head_dim);
+    koff[n] = swz_slot_offset((wave + NW * n) * 64 + lane, BN, G::KSLOTS, 4 * DBLK, a.k_ss,
+                              a.head_dim);
 #pragma unroll
   for (int n = 0; n < G::VPER; ++n)
     voff[n] = tile_slot_offset((wave + NW * n) * 64 + lane, BN, G::VSLOTS, a.v_ss, a.head_dim);
@@ -261,10 +268,18 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) acc[db] = (f32x16_t){};
 
-  const int k_lane = l32 * KR + hi * 16;  // b128 row reads of K
-  const int v_lane = l32 * VR + hi * 16;  // b128 row reads of V
+  // b128 row reads of K (row l32 of a 32-row block, chunk 2 st + hi; even
+  // and odd k-steps differ in bit 1 of the swizzled chunk) and of V
+  const int sw = (l32 >> 2) & 3;
+  const int k_even = l32 * KR + 16 * (hi ^ sw), k_odd = l32 * KR + 16 * (hi ^ sw ^ 2);
+  const int v_lane = l32 * VR + hi * 16;
+  // transposing reads of K: rows 16 u + 4 hi + s16 / 4 (swizzle hi) and 8
+  // rows further (swizzle hi ^ 2), chunk 4 db + 2 ((lane / 16) % 2) + (s16 % 4) / 2
   const int s16 = lane & 15;
-  const int t_lane = (4 * hi + (s16 >> 2)) * KR + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+  const int t_row = 4 * hi + (s16 >> 2);
+  const int t_ch = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1), t_half = 8 * (s16 & 1);
+  const int t_lo = t_row * KR + 16 * (t_ch ^ hi) + t_half;
+  const int t_up = (t_row + 8) * KR + 16 * (t_ch ^ hi ^ 2) + t_half;
 
   // one key tile; its K / V are in stage kb, the next tile loads into nb
   auto step = [&](int t, FA_LDS char* kb, FA_LDS char* nb) {
@@ -282,7 +297,8 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
     for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const frag kf = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(kb + k_lane + kb2 * 32 * KR + st * 32));
+        const frag kf = __builtin_bit_cast(
+            frag, *(FA_LDS u32x4_t*)(kb + ((st & 1) ? k_odd : k_even) + kb2 * 32 * KR + 64 * (st >> 1)));
         const frag vf = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(vb + v_lane + kb2 * 32 * VR + st * 32));
         s[kb2] = M::mma(kf, qf[st], s[kb2]);
         dp[kb2] = M::mma(vf, dof[st], dp[kb2]);
@@ -314,9 +330,9 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
       const frag sf = __builtin_bit_cast(frag, sraw);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        FA_LDS char* p0 = kb + t_lane + (16 * u) * KR + db * 64;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p0);
-        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + 8 * KR));
+        FA_LDS char* p0 = kb + (16 * u) * KR + db * 64;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + t_lo));
+        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + t_up));
         const u32x4_t kraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
                               __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
         acc[db] = M::mma(__builtin_bit_cast(frag, kraw), sf, acc[db]);
@@ -365,7 +381,7 @@ struct BwdKVTile {
   static constexpr int BQ = 32;                  // queries per streamed tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = (D + 31) / 32;
-  static constexpr int QR = dual_stride(D * 2);  // Q / dO rows: b128 + transposed
+  static constexpr int QR = tr_row_stride(DBLK * 64);  // Q / dO rows: b128 + transposed, swizzled
   static constexpr int QSLOTS = QR / 16;
   static constexpr int QINSTR = (BQ * QSLOTS + 63) / 64;  // wave-wide loads per tile
   static constexpr int QPER = (QINSTR + NW - 1) / NW;
@@ -455,8 +471,8 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
 #pragma unroll
   for (int n = 0; n < G::QPER; ++n) {
     const int slot = (wave + NW * n) * 64 + lane;
-    qoff[n] = tile_slot_offset(slot, BQ, G::QSLOTS, a.q_ss, a.head_dim);
-    doff[n] = tile_slot_offset(slot, BQ, G::QSLOTS, a.do_ss, a.head_dim);
+    qoff[n] = swz_slot_offset(slot, BQ, G::QSLOTS, 4 * DBLK, a.q_ss, a.head_dim);
+    doff[n] = swz_slot_offset(slot, BQ, G::QSLOTS, 4 * DBLK, a.do_ss, a.head_dim);
   }
   auto issue = [&](int j, FA_LDS char* qb) {
     const int qa = j * BQ;
@@ -482,11 +498,15 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     dkacc[db] = (f32x16_t){};
   }
 
-  const int q_lane = l32 * QR + hi * 16;                          // b128 row reads of Q / dO
+  // b128 row reads of Q / dO (row l32, chunk 2 st + hi, swizzled) and
+  // transposing reads (rows 16 u + 4 hi + s16 / 4 and 8 rows further)
+  const int sw = (l32 >> 2) & 3;
+  const int q_even = l32 * QR + 16 * (hi ^ sw), q_odd = l32 * QR + 16 * (hi ^ sw ^ 2);
   const int s16 = lane & 15;
-  const int t_row = 4 * hi + (s16 >> 2);                          // transposing reads
-  const int t_col = (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
-  const int t_lane = t_row * QR + t_col;
+  const int t_row = 4 * hi + (s16 >> 2);
+  const int t_ch = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1), t_half = 8 * (s16 & 1);
+  const int t_lo = t_row * QR + 16 * (t_ch ^ hi) + t_half;
+  const int t_up = (t_row + 8) * QR + 16 * (t_ch ^ hi ^ 2) + t_half;
 
   // lse * log2e and delta of query tile j: wave 0 loads them (lane = row,
   // index clamped) while the tile before it is processed, and stores them
@@ -522,8 +542,9 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      const frag qfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + q_lane + st * 32));
-      const frag dfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + q_lane + st * 32));
+      const int qo = ((st & 1) ? q_odd : q_even) + 64 * (st >> 1);
+      const frag qfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + qo));
+      const frag dfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + qo));
       s = M::mma(qfr, kf[st], s);
       if constexpr (G::V_IN_LDS) {
         const frag vfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(v_lds + v_lane + st * 32));
@@ -565,12 +586,12 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
       const frag sfr = __builtin_bit_cast(frag, (u32x4_t){ps[4 * u], ps[4 * u + 1], ps[4 * u + 2], ps[4 * u + 3]});
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        FA_LDS char* d0 = dob + t_lane + (16 * u) * QR + db * 64;
-        FA_LDS char* q0p = qb + t_lane + (16 * u) * QR + db * 64;
-        const i16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)d0);
-        const i16x4_t dup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(d0 + 8 * QR));
-        const i16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)q0p);
-        const i16x4_t qup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(q0p + 8 * QR));
+        FA_LDS char* d0 = dob + (16 * u) * QR + db * 64;
+        FA_LDS char* q0p = qb + (16 * u) * QR + db * 64;
+        const i16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(d0 + t_lo));
+        const i16x4_t dup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(d0 + t_up));
+        const i16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(q0p + t_lo));
+        const i16x4_t qup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(q0p + t_up));
         const u32x4_t draw = {__builtin_bit_cast(u32x2_t, dlo)[0], __builtin_bit_cast(u32x2_t, dlo)[1],
                               __builtin_bit_cast(u32x2_t, dup)[0], __builtin_bit_cast(u32x2_t, dup)[1]};
         const u32x4_t qraw = {__builtin_bit_cast(u32x2_t, qlo)[0], __builtin_bit_cast(u32x2_t, qlo)[1],
