@@ -61,10 +61,6 @@ fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& 
 }
 
 // Instantiated head-dim paddings: the smallest one >= head_dim is used.
-#ifndef FA_OCC16
-#define FA_OCC16 2  // waves per SIMD the register budget is sized for
-#endif
-
 template <typename T, int D, int NW, int OCC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_16bit(fa::FwdArgs a) {
@@ -76,7 +72,7 @@ void fa_fwd_16bit(fa::FwdArgs a) {
 // used when the 8-wave grid would be too small to fill the 256 CUs well.
 template <typename T, int NW>
 fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
-  constexpr int OCC = FA_OCC16;
+  constexpr int OCC = 2;  // waves per SIMD the register budget is sized for
   a.n_qtiles = (int32_t)((a.seq_q + 32 * NW - 1) / (32 * NW));
   const int64_t grid = (int64_t)a.n_bh * a.n_qtiles * a.n_splits;
   if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
@@ -99,13 +95,8 @@ fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
 
 // Waves per workgroup of the 16-bit forward (8 when the grid stays large).
 int waves_16bit(int64_t n_bh, int64_t seq_q, int64_t head_dim) {
-#ifdef FA_FORCE_NW16
-  (void)n_bh; (void)seq_q; (void)head_dim;
-  return FA_FORCE_NW16;
-#else
   if (head_dim > 128) return 4;
   return n_bh * ((seq_q + 255) / 256) >= 1024 ? 8 : 4;
-#endif
 }
 
 template <typename T>
