@@ -32,7 +32,12 @@ __device__ inline f32x16_t mma_e5m2(const i32x8_t& a, const i32x8_t& b, const f3
 
 // four floats -> four e5m2 bytes (round to nearest even), x0 in the low byte
 __device__ inline uint32_t pack4_e5m2(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, 0, false);
+  // the first conversion writes bytes 0-1 and keeps bytes 2-3 of its old
+  // value, which the second overwrites: start from an unspecified register
+  // instead of materialising a zero
+  int w;
+  asm volatile("" : "=v"(w));
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, w, false);
   w = __builtin_amdgcn_cvt_pk_bf8_f32(x2, x3, w, true);
   return (uint32_t)w;
 }
@@ -211,7 +216,7 @@ __device__ __forceinline__ void fa_fwd_e5m2_body(const FwdArgs& a) {
   // P = exp2(s c - m) in e5m2: bytes 0..15 keys 16 hi + r (block 0), 16..31 block 1
   auto probs = [&](const f32x16_t (&s)[2], i32x8_t& pf) {
     const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float part[4];  // four partial sums, each started by its first term
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -220,7 +225,10 @@ __device__ __forceinline__ void fa_fwd_e5m2_body(const FwdArgs& a) {
         const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
         const float p2 = fast_exp2(__builtin_fmaf(s[kb2][r + 2], c, -msub));
         const float p3 = fast_exp2(__builtin_fmaf(s[kb2][r + 3], c, -msub));
-        part[r >> 2] += (p0 + p1) + (p2 + p3);
+        if (kb2 == 0)
+          part[r >> 2] = (p0 + p1) + (p2 + p3);
+        else
+          part[r >> 2] += (p0 + p1) + (p2 + p3);
         pf[4 * kb2 + (r >> 2)] = (int32_t)pack4_e5m2(p0, p1, p2, p3);
       }
     l_run += (part[0] + part[1]) + (part[2] + part[3]);
