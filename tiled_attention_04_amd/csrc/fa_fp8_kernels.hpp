@@ -165,7 +165,10 @@ __device__ __forceinline__ void fa_fwd_e5m2_body(const FwdArgs& a) {
   f32x16_t acc[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) acc[db] = (f32x16_t){};
-  float m_run = -INFINITY, l_run = 0.f;
+  // reference max starts at the lowest finite value rather than -inf: the first
+  // tile with any visible key replaces it (alpha = 0), and exp2(s c - m_run)
+  // needs no guard against -inf - (-inf)
+  float m_run = -__FLT_MAX__, l_run = 0.f;
   const float c = a.c;
   const int k_lane = l32 * KROW + hi * 32;  // A operand of S^T: LDS row l32 (+32 kb2), 32 bytes
   const int v_lane = l32 * VROW + hi * 16;  // A operand of O^T: dim row l32 (+32 db), keys 16h.., 32+16h..
@@ -215,7 +218,7 @@ __device__ __forceinline__ void fa_fwd_e5m2_body(const FwdArgs& a) {
 
   // P = exp2(s c - m) in e5m2: bytes 0..15 keys 16 hi + r (block 0), 16..31 block 1
   auto probs = [&](const f32x16_t (&s)[2], i32x8_t& pf) {
-    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+    const float msub = m_run;
     float part[4];  // four partial sums, each started by its first term
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
