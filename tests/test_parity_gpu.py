@@ -64,13 +64,13 @@ def test_ragged_sequences(dtype, causal, sq, sk):
     full_parity(synth.make_inputs(w), name=f"ragged {dtype} sq={sq} sk={sk} causal={causal}")
 
 
-@pytest.mark.parametrize("d", [8, 16, 24, 32, 40, 64, 72, 80, 96, 112, 128, 136, 160, 192, 256])
+@pytest.mark.parametrize("d", [8, 16, 24, 32, 40, 64, 72, 80, 96, 112, 128, 136, 160, 192, 200, 256])
 def test_head_dims_bf16(d):
     w = synth.custom("hd", "bf16", "bhsd", 1, 2, 150, 190, d, causal=(d % 16 == 0), seed=200 + d)
     full_parity(synth.make_inputs(w), name=f"head_dim bf16 d={d}")
 
 
-@pytest.mark.parametrize("d", [8, 64, 80, 128])
+@pytest.mark.parametrize("d", [8, 64, 80, 128, 248])
 def test_head_dims_fp16(d):
     w = synth.custom("hd", "fp16", "bhsd", 1, 2, 150, 190, d, causal=True, seed=300 + d)
     full_parity(synth.make_inputs(w), name=f"head_dim fp16 d={d}")

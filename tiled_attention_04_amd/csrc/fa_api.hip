@@ -61,10 +61,10 @@ fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& 
 }
 
 // Instantiated head-dim paddings: the smallest one >= head_dim is used.
-template <typename T, int D, int NW, int OCC>
+template <typename T, int D, int NW, int OCC, int DV = D>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_16bit(fa::FwdArgs a) {
-  fa::fa_fwd_16bit_body<T, D, NW>(a);
+  fa::fa_fwd_16bit_body<T, D, NW, DV>(a);
 }
 
 // Workgroups of 8 waves (256 query rows) halve the K/V traffic per query and
@@ -88,8 +88,16 @@ fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   a4.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
   const int64_t grid4 = (int64_t)a.n_bh * a4.n_qtiles * a.n_splits;
   if (grid4 > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid4);
-  FA_CASE(160) FA_CASE(192) FA_CASE(256)
+  FA_CASE(160) FA_CASE(192)
 #undef FA_CASE
+  if (head_dim <= 256) {
+    // one pass at D = 256 spills registers: two passes, each contracting the
+    // scores over all dims and forming 128 of the output dims
+    const fa_status_t st = launch(fa_fwd_16bit<T, 256, 4, 1, 128>, grid4, 256, a4, stream);
+    if (st != FA_OK) return st;
+    a4.v_col0 = 128;
+    return launch(fa_fwd_16bit<T, 256, 4, 1, 128>, grid4, 256, a4, stream);
+  }
   return fail(FA_ERR_HEAD_DIM, "head_dim %lld unsupported", (long long)head_dim);
 }
 
