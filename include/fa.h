@@ -109,6 +109,9 @@ typedef struct {
  *   q/k/v/o NULL                                 -> FA_ERR_NULL
  *   a base pointer not 16-byte aligned (f16/bf16/e5m2) or 4-byte aligned (f32),
  *   lse not 4-byte aligned                       -> FA_ERR_LAYOUT
+ *   a launch of more than 2^32 - 1 work-items (workgroups x threads; one
+ *   dispatch counts work-items in 32 bits), e.g. batch * heads * seq_q of
+ *   2^31 or more                                 -> FA_ERR_SHAPE
  * A failed launch returns FA_ERR_HIP.  On any non-OK return nothing has been
  * enqueued and fa_last_error() describes the problem.
  */
@@ -138,7 +141,9 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * Key splitting needs bf16/fp16 (fp32 or e5m2 with num_splits > 1 ->
  * FA_ERR_DTYPE; num_splits outside 0..16 -> FA_ERR_WORKSPACE; both checked
  * right after the dtype); a missing/misaligned/short workspace ->
- * FA_ERR_WORKSPACE (checked after the fa_fwd checks, before any HIP call).
+ * FA_ERR_WORKSPACE (checked after the fa_fwd checks, before any HIP call);
+ * a split launch or the merge launch (8 threads per query row) beyond 2^32 - 1
+ * work-items -> FA_ERR_SHAPE, before anything is enqueued.
  * O is rounded once, after the merge.  Two calls that share a workspace on
  * different streams race.
  */
@@ -201,8 +206,11 @@ size_t fa_fwd_splitk_workspace(int64_t batch, int64_t heads, int64_t seq_q, int6
  * -> FA_OK with nothing launched; k, v, dk, dv NULL, or (seq_q > 0) q, o,
  * dout, lse, delta, dq NULL -> FA_ERR_NULL; a tensor not 16-byte aligned
  * (16-bit) or 4-byte aligned (fp32), or lse/delta not 4-byte aligned ->
- * FA_ERR_LAYOUT.  If a launch fails
- * (FA_ERR_HIP) the launches before it in this call stay enqueued.
+ * FA_ERR_LAYOUT; any of the three launches beyond 2^32 - 1 work-items (the
+ * delta launch runs 8 threads per query row, so batch * heads * seq_q of
+ * 2^29 or more) -> FA_ERR_SHAPE, all checked before the first is enqueued.
+ * If a launch fails (FA_ERR_HIP) the launches before it in this call stay
+ * enqueued.
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, float* delta, void* dq, void* dk, void* dv,

@@ -177,3 +177,46 @@ def test_splitk_sizes_and_choice():
     assert fa.fa_fwd_splitk_choose(0, 1, 10, 10, 64, 0) == 1
     # an empty problem needs no workspace
     assert call_splitk(batch=0, ws=None, q=None, k=None, v=None, o=None) == 0
+
+
+def _contig(seq, heads, d=8):
+    return S(heads * seq * d, seq * d, d, 1)
+
+
+def test_fwd_rejects_dispatch_beyond_32bit_work_items():
+    # 65536 heads x 128 tiles of 256 queries x 512 threads = 2^32 work-items
+    st = _contig(32768, 65536)
+    rc = fa.fa_fwd(P, P, P, P, None, 1, 65536, 32768, 32768, 8, st, st, st, st, 0.125, 0, BF16,
+                   None)
+    assert rc == 2, (rc, fa.last_error())
+    assert "work-items" in fa.last_error()
+
+
+def test_splitk_rejects_merge_beyond_32bit_work_items_before_launching():
+    # 2^29 query rows: the split launch fits (2^31 work-items) but the merge
+    # (8 threads per row) would need 2^32, so nothing may be enqueued
+    st = _contig(32768, 16384)
+    rc = fa.fa_fwd_splitk(P, P, P, P, None, 1, 16384, 32768, 32768, 8, st, st, st, st, 0.125, 0,
+                          BF16, 2, P, 1 << 40, None)
+    assert rc == 2, (rc, fa.last_error())
+    assert "work-items" in fa.last_error()
+
+
+def test_bwd_rejects_delta_launch_beyond_32bit_work_items():
+    sq = _contig(32768, 16384)
+    sk = _contig(128, 16384)
+    rc = fa.fa_bwd(P, P, P, P, P, P, P, P, P, P, 1, 16384, 32768, 128, 8,
+                   sq, sk, sk, sq, sq, sq, sk, sk, 0.125, 0, BF16, None)
+    assert rc == 2, (rc, fa.last_error())
+    assert "work-items" in fa.last_error()
+
+
+def test_bwd_rejects_key_launch_beyond_32bit_work_items():
+    # 2 heads of 2^31 - 512 keys: dK/dV needs 2 threads per key and head
+    n = (1 << 31) - 512
+    sq = _contig(128, 2)
+    sk = _contig(n, 2)
+    rc = fa.fa_bwd(P, P, P, P, P, P, P, P, P, P, 1, 2, 128, n, 8,
+                   sq, sk, sk, sq, sq, sq, sk, sk, 0.125, 0, BF16, None)
+    assert rc == 2, (rc, fa.last_error())
+    assert "work-items" in fa.last_error()

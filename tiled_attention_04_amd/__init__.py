@@ -110,6 +110,34 @@ def last_error():
     return lib().fa_last_error().decode()
 
 
+def _check_device(device, **tensors):
+    """Every tensor given must live on `device` (a CUDA device): a host
+    pointer handed to a kernel would fault the GPU, so nothing is launched."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor (got {t.device})")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, q on {device}")
+
+
+def _check_like(name, t, shape, dtype):
+    """A caller-supplied output: exactly `shape` and `dtype` (the C ABI cannot
+    see sizes, so an undersized buffer would be written past its end)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _check_rows(name, t, B, H, Sq):
+    """lse / delta: contiguous fp32 [B, H, Sq]."""
+    import torch
+    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, Sq) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 [{B}, {H}, {Sq}] tensor")
+
+
 def _dtype_code(t):
     import torch
     codes = {torch.float32: FA_DTYPE_F32, torch.float16: FA_DTYPE_F16,
@@ -164,8 +192,9 @@ def forward(q, k, v, causal=False, sm_scale=None, layout="bhsd", out=None, lse=N
     return_lse is False (then lse is not computed unless passed in).
     """
     import torch
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not q.is_cuda:
         raise ValueError("q, k and v must be device tensors")
+    _check_device(q.device, k=k, v=v, out=out, lse=lse)
     (B, H, Sq, D), q_st = _dims(q, layout)
     (Bk, Hk, Sk, Dk), k_st = _dims(k, layout)
     if q.dtype == torch.float8_e5m2:
@@ -184,9 +213,12 @@ def forward(q, k, v, causal=False, sm_scale=None, layout="bhsd", out=None, lse=N
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    _check_like("out", out, q.shape, q.dtype)
     (_, _, _, _), o_st = _dims(out, layout)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_rows("lse", lse, B, H, Sq)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                 lse.data_ptr() if lse is not None else None, B, H, Sq, Sk, D,
@@ -203,22 +235,31 @@ def forward_splitk(q, k, v, causal=False, sm_scale=None, layout="bhsd", num_spli
     device tensor of at least fa_fwd_splitk_workspace(...) bytes (allocated
     when None).  Returns (o, lse)."""
     import torch
+    if not q.is_cuda:
+        raise ValueError("q, k and v must be device tensors")
+    _check_device(q.device, k=k, v=v, out=out, lse=lse, workspace=workspace)
     (B, H, Sq, D), q_st = _dims(q, layout)
     (Bk, Hk, Sk, Dk), k_st = _dims(k, layout)
     (Bv, Hv, Sv, Dv), v_st = _dims(v, layout)
     if (Bk, Hk, Dk) != (B, H, D) or (Bv, Hv, Sv, Dv) != (B, H, Sk, D):
         raise ValueError("q, k, v shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     if num_splits == 0:
         num_splits = fa_fwd_splitk_choose(B, H, Sq, Sk, D, causal)
     out = torch.empty_like(q) if out is None else out
+    _check_like("out", out, q.shape, q.dtype)
     (_, _, _, _), o_st = _dims(out, layout)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _check_rows("lse", lse, B, H, Sq)
     need = fa_fwd_splitk_workspace(B, H, Sq, D, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -240,9 +281,9 @@ def backward(q, k, v, o, dout, lse, causal=False, sm_scale=None, layout="bhsd",
     receives rowsum(dout * o).
     """
     import torch
-    for t in (q, k, v, o, dout, lse):
-        if not t.is_cuda:
-            raise ValueError("all tensors must be device tensors")
+    if not q.is_cuda:
+        raise ValueError("all tensors must be device tensors")
+    _check_device(q.device, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta)
     (B, H, Sq, D), q_st = _dims(q, layout)
     (Bk, Hk, Sk, Dk), k_st = _dims(k, layout)
     (_, _, Sv, _), v_st = _dims(v, layout)
@@ -252,15 +293,18 @@ def backward(q, k, v, o, dout, lse, causal=False, sm_scale=None, layout="bhsd",
         raise ValueError("q, k, v, o, dout shapes disagree")
     if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
         raise TypeError("q, k, v, o and dout must share a dtype")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, H, Sq] tensor")
+    _check_rows("lse", lse, B, H, Sq)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_like("dq", dq, q.shape, q.dtype)
+    _check_like("dk", dk, k.shape, q.dtype)
+    _check_like("dv", dv, v.shape, q.dtype)
     if delta is None:
         delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _check_rows("delta", delta, B, H, Sq)
     (_, _, _, _), dq_st = _dims(dq, layout)
     (_, _, _, _), dk_st = _dims(dk, layout)
     (_, _, _, _), dv_st = _dims(dv, layout)

@@ -50,8 +50,20 @@ fa_status_t check_strides(const char* name, const fa_strides_t& st, int64_t mult
   return FA_OK;
 }
 
+// One dispatch covers at most 2^32 - 1 work-items (the packet's grid size
+// is a 32-bit count of work-items, not of workgroups).
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+
+fa_status_t check_dispatch(int64_t grid, int threads) {
+  if (grid > kInt32Max || grid * threads > kMaxWorkItems)
+    return fail(FA_ERR_SHAPE, "a launch of %lld workgroups x %d threads exceeds the 2^32 work-items of one dispatch",
+                (long long)grid, threads);
+  return FA_OK;
+}
+
 template <typename Kernel>
 fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& args, void* stream) {
+  if (fa_status_t s = check_dispatch(grid, threads)) return s;
   fa::FwdArgs a = args;
   void* params[] = {&a};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)grid),
@@ -135,6 +147,7 @@ size_t splitk_workspace_bytes(int64_t n_bh, int64_t seq_q, int64_t head_dim, int
 template <typename T>
 fa_status_t launch_combine(const fa::FwdArgs& a, void* stream) {
   const int64_t rows = (int64_t)a.n_bh * a.seq_q;
+  if (fa_status_t s = check_dispatch((rows + 31) / 32, 256)) return s;
   fa::FwdArgs c = a;
   void* params[] = {&c};
   const void* kernel = a.n_splits <= 2   ? reinterpret_cast<const void*>(fa::fa_fwd_combine<T, 2>)
@@ -239,7 +252,7 @@ void fa_bwd_dkv_f32(fa::BwdArgs a) {
 template <typename Kernel>
 fa_status_t launch_bwd(Kernel kernel, int64_t grid, int threads, const fa::BwdArgs& args,
                        void* stream) {
-  if (grid > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
+  if (fa_status_t s = check_dispatch(grid, threads)) return s;
   fa::BwdArgs a = args;
   void* params[] = {&a};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)grid),
@@ -397,6 +410,10 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     a.part_o = (float*)workspace;
     a.part_lse = a.part_o + (size_t)splits * (size_t)(batch * heads) * (size_t)seq_q * (size_t)head_dim;
   }
+  // the merge runs after the split shares: bound its dispatch before any launch
+  if (splits > 1) {
+    if (fa_status_t s2 = check_dispatch((batch * heads * seq_q + 31) / 32, 256)) return s2;
+  }
   fa_status_t st;
   switch (dtype) {
     case FA_DTYPE_BF16:
@@ -489,6 +506,19 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
       return fail(FA_ERR_LAYOUT, "%s must be %d-byte aligned", names[i], (int)align);
   if ((lse && !aligned(lse, 4)) || (delta && !aligned(delta, 4)))
     return fail(FA_ERR_LAYOUT, "lse and delta must be 4-byte aligned");
+
+  // bound all three dispatches before the first is enqueued: delta (8 lanes
+  // per query row), dQ (128-query blocks of 256 threads), dK/dV (at most 2
+  // threads per key: 256-key blocks of 512 or 128-key blocks of 256)
+  {
+    const int64_t bh = batch * heads;
+    if (seq_q > 0) {
+      if (fa_status_t s2 = check_dispatch((bh * seq_q + 31) / 32, 256)) return s2;
+      if (fa_status_t s2 = check_dispatch(bh * ((seq_q + 127) / 128), 256)) return s2;
+    }
+    if (fa_status_t s2 = check_dispatch(bh * ((seq_k + 255) / 256), 512)) return s2;
+    if (fa_status_t s2 = check_dispatch(bh * ((seq_k + 127) / 128), 256)) return s2;
+  }
 
   fa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
