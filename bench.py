@@ -14,8 +14,16 @@ Prints one JSON line:
   cpu_baseline  the CPU oracle (C, double, OpenMP) timed on a bounded sample
              of the same workload on this host
 
+The default line also carries `parity`: the max-abs and mean-abs error of the
+timed run's O and lse against the oracle on the rows the CPU baseline ran.
+
 Other modes:
-  --workload c2|c3|c4   time another workload (not the default line); also
+  --all-configs         one JSON line per workload C1..C5 (the five configs:
+                        ms, TFLOP/s, % of peak, HBM traffic when counted on the
+                        current source, and the error of that run's output
+                        against the oracle over EVERY row; C5's oracle runs in
+                        chunks of heads, about a minute on 16 host cores)
+  --workload c1|c2|c3|c4   time another workload (not the default line); also
                         short100 / short10 (few queries against 4096 keys) and
                         c5_e5m2 (the default workload in float8 e5m2, V passed
                         key-major; roofline against the dense fp8 MFMA peak)
@@ -46,7 +54,7 @@ PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (1 GPU)"
 KERNEL_SOURCES = ["tiled_attention_04_amd/csrc/fa_fwd_kernels.hpp",
                   "tiled_attention_04_amd/csrc/fa_api.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c5.json")
+PROFILES = os.path.join(ROOT, "profiles")
 # context only: the pages' unfused attention timings on an RTX 3090 (fp32,
 # d_model 768, 12 heads, batch 4; sequence length not stated)
 CONTEXT_RTX3090 = {"qk_matmul_ms": 0.1428, "pv_matmul_ms": 0.0759, "softmax_ms": 0.0314,
@@ -61,11 +69,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per launch from the committed counter summary, if it matches
-    the current kernel source; otherwise None."""
+def load_traffic(key="c5"):
+    """HBM bytes per launch of workload `key` from the committed counter
+    summary profiles/traffic_<key>.json, if it matches the current kernel
+    source; otherwise None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"traffic_{key}.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -91,6 +100,8 @@ def cpu_baseline(inp, target_s=15.0):
         keys = np.minimum(i + 1, w.seq_k) if w.causal else np.full(rows.shape, w.seq_k)
         return float(np.sum(4.0 * keys * w.head_dim))
 
+    ref = {}
+
     def run(n_heads, n_rows):
         heads = [(bh // w.heads, bh % w.heads) for bh in range(n_heads)]
         q64 = inp.as_bhsd_f64("q", heads)
@@ -98,7 +109,7 @@ def cpu_baseline(inp, target_s=15.0):
         v64 = inp.as_bhsd_f64("v", heads)
         rows = np.unique(np.linspace(0, n_heads * S - 1, n_rows).astype(np.int64))
         t0 = time.perf_counter()
-        oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=rows)
+        ref["o"], ref["lse"] = oracle.forward_rows(q64, k64, v64, w.sm_scale, w.causal, rows=rows)
         return rows, time.perf_counter() - t0
 
     mean_row = 4.0 * w.head_dim * ((w.seq_k + 1) / 2 if w.causal else w.seq_k)
@@ -117,7 +128,9 @@ def cpu_baseline(inp, target_s=15.0):
                      f"pairs of the same workload (fp64 C oracle, materialised softmax), "
                      f"{dt:.1f} s wall"}
     out["numpy_oracle"] = numpy_oracle_rate(inp)
-    return out
+    # rows are flat ids of the first n_heads (batch, head) pairs, hence of the
+    # whole problem too: the caller compares the GPU output on them
+    return out, rows, ref["o"], ref["lse"]
 
 
 def numpy_oracle_rate(inp, max_rows=8192):
@@ -213,13 +226,188 @@ def bench_bwd(args, w, inp, up, q, k, v, o, lse, layout, stream):
     return 0
 
 
+def upload(w, a, dev):
+    import numpy as np
+    import torch
+    if w.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    if w.dtype == "e5m2":
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e5m2).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_bhsd_f64(t, layout):
+    """A device output ([B,H,S,...] or [S,H,...] for "shd") as float64 [B,H,S,...]."""
+    import numpy as np
+    import torch
+    x = t.detach().to(torch.float64).cpu().numpy()
+    if layout == "shd":
+        x = np.moveaxis(x, 0, 1)[None] if x.ndim == 3 else x
+    return x
+
+
+def error_summary(o_gpu, lse_gpu, o_ref, lse_ref, rows, how):
+    """Max-abs and mean-abs errors of O and lse (float64 arrays of equal shape)."""
+    import numpy as np
+    eo, el = np.abs(o_gpu - o_ref), np.abs(lse_gpu - lse_ref)
+    return {"o_max_abs": float(eo.max()), "o_mean_abs": float(eo.mean()),
+            "lse_max_abs": float(el.max()), "lse_mean_abs": float(el.mean()),
+            "rows": int(rows), "finite": bool(np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all()),
+            "against": how}
+
+
+def whole_output_errors(w, inp, o, lse, layout, heads_per_chunk):
+    """Error of the GPU output over every row, the oracle run a few heads at a time."""
+    import numpy as np
+    import oracle
+    o_all = to_bhsd_f64(o, layout)
+    lse_all = lse.detach().double().cpu().numpy()
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    acc = {"o_max": 0.0, "o_sum": 0.0, "l_max": 0.0, "l_sum": 0.0}
+    t0 = time.perf_counter()
+    for c in range(0, len(pairs), heads_per_chunk):
+        chunk = pairs[c:c + heads_per_chunk]
+        o_ref, lse_ref = oracle.forward(inp.as_bhsd_f64("q", chunk), inp.as_bhsd_f64("k", chunk),
+                                        inp.as_bhsd_f64("v", chunk), w.sm_scale, w.causal)
+        eo = np.abs(np.stack([o_all[b, h] for (b, h) in chunk])[:, None] - o_ref)
+        el = np.abs(np.stack([lse_all[b, h] for (b, h) in chunk])[:, None] - lse_ref)
+        acc["o_max"], acc["o_sum"] = max(acc["o_max"], float(eo.max())), acc["o_sum"] + float(eo.sum())
+        acc["l_max"], acc["l_sum"] = max(acc["l_max"], float(el.max())), acc["l_sum"] + float(el.sum())
+        print(f"[bench] {w.name}: oracle over heads {c}..{c + len(chunk) - 1} of {len(pairs)} "
+              f"({time.perf_counter() - t0:.0f} s)", file=sys.stderr, flush=True)
+    return {"o_max_abs": acc["o_max"], "o_mean_abs": acc["o_sum"] / o_all.size,
+            "lse_max_abs": acc["l_max"], "lse_mean_abs": acc["l_sum"] / lse_all.size,
+            "rows": int(lse_all.size),
+            "finite": bool(np.isfinite(o_all).all() and np.isfinite(lse_all).all()),
+            "against": "fp64 C oracle, every row", "oracle_s": round(time.perf_counter() - t0, 1)}
+
+
+def time_launches(step, stream, steps, warmup):
+    """W untimed launches, then K timed ones: events around the region and
+    around every launch.  Returns (ms per step over the region, sorted
+    per-launch ms, wall seconds)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    per_launch = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    return region0.elapsed_time(region1) / steps, per_launch, t_wall
+
+
+def bench_line(w, key, steps, warmup, splits, ms_per_step, per_launch, peak):
+    flops = w.flops()
+    ms_avg = sum(per_launch) / len(per_launch)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (ms_avg * 1e-3) / 1e12
+    return {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "key_splits": splits, "batch": w.batch, "heads": w.heads,
+                   "seq_q": w.seq_q, "seq_k": w.seq_k, "head_dim": w.head_dim,
+                   "causal": w.causal, "sm_scale": w.sm_scale, "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": load_traffic(key) if splits == 1 else None,
+                     "kernel_ms_avg": round(ms_avg, 5),
+                     "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
+                     "kernel_ms_min": round(per_launch[0], 5)},
+        "context": {"rtx3090_unfused_per_call": CONTEXT_RTX3090},
+    }
+
+
+class Setup:
+    """Seeded inputs of one workload, resident on the device, and its step."""
+
+    def __init__(self, key, dev, splits=1):
+        import torch
+        import tiled_attention_04_amd as fa
+        from tiled_attention_04_amd import synth
+        w = synth.WORKLOADS.get(key) or synth.EXTRA_WORKLOADS[key]
+        print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+        self.key, self.w, self.inp = key, w, synth.make_inputs(w)
+        q, k = upload(w, self.inp.q, dev), upload(w, self.inp.k, dev)
+        if w.dtype == "e5m2":
+            import numpy as np
+            # the fp8 path takes V key-major: [B, H, D, Sk] (Sk is a multiple of 16 here)
+            v = upload(w, np.transpose(self.inp.v, (0, 1, 3, 2)), dev)
+        else:
+            v = upload(w, self.inp.v, dev)
+        self.q, self.k, self.v = q, k, v
+        self.peak = PEAK_FP8_TFLOPS if w.dtype == "e5m2" else PEAK_BF16_TFLOPS
+        self.layout = layout = "shd" if w.layout == "shd" else "bhsd"
+        self.o = o = torch.empty_like(q)
+        self.lse = lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.splits = 1
+        if splits != 1:
+            self.splits = splits or fa.fa_fwd_splitk_choose(w.batch, w.heads, w.seq_q, w.seq_k,
+                                                            w.head_dim, w.causal)
+            ws = torch.empty(max(1, fa.fa_fwd_splitk_workspace(w.batch, w.heads, w.seq_q,
+                                                               w.head_dim, self.splits)),
+                             dtype=torch.uint8, device=dev)
+            n = self.splits
+
+            def step():
+                fa.forward_splitk(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout,
+                                  num_splits=n, out=o, lse=lse, workspace=ws)
+        else:
+            def step():
+                fa.forward(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout, out=o,
+                           lse=lse)
+        self.step = step
+
+
+def all_configs(args, dev):
+    """One line per workload C1..C5, each with the whole-output error of its run."""
+    import torch
+    for key in ("c1", "c2", "c3", "c4", "c5"):
+        st = Setup(key, dev)
+        ms, per, _ = time_launches(st.step, st.stream, args.steps, args.warmup)
+        out = bench_line(st.w, key, args.steps, args.warmup, 1, ms, per, st.peak)
+        print(f"[bench] {key}: {ms:.4f} ms/step, kernel min {per[0]:.4f} ms",
+              file=sys.stderr, flush=True)
+        # the output of the last timed launch, against the oracle over every row
+        out["parity"] = whole_output_errors(st.w, st.inp, st.o, st.lse, st.layout,
+                                            heads_per_chunk=2 if key == "c5" else 16)
+        print(json.dumps(out), flush=True)
+        del st
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c5",
-                    choices=["c2", "c3", "c4", "c5", "short100", "short10", "c5_e5m2"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "short100", "short10", "c5_e5m2"])
+    ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-pmc", default=None)
@@ -238,86 +426,28 @@ def main():
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import tiled_attention_04_amd as fa
-    from tiled_attention_04_amd import synth
 
     fa.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS.get(args.workload) or synth.EXTRA_WORKLOADS[args.workload]
-    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(w)
+    if args.all_configs:
+        return all_configs(args, dev)
 
-    def up(a):
-        if w.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
-                torch.bfloat16).to(dev)
-        if w.dtype == "e5m2":
-            return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e5m2).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    q, k = up(inp.q), up(inp.k)
-    if w.dtype == "e5m2":
-        # the fp8 path takes V key-major: [B, H, D, Sk] (Sk is a multiple of 16 here)
-        v = up(np.transpose(inp.v, (0, 1, 3, 2)))
-    else:
-        v = up(inp.v)
-    peak = PEAK_FP8_TFLOPS if w.dtype == "e5m2" else PEAK_BF16_TFLOPS
-    layout = "shd" if w.layout == "shd" else "bhsd"
-    o = torch.empty_like(q)
-    lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        fa.forward(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout, out=o, lse=lse)
-
-    splits = 1
-    if args.splits != 1 and args.which == "fwd":
-        splits = args.splits or fa.fa_fwd_splitk_choose(w.batch, w.heads, w.seq_q, w.seq_k,
-                                                         w.head_dim, w.causal)
-        ws = torch.empty(max(1, fa.fa_fwd_splitk_workspace(w.batch, w.heads, w.seq_q,
-                                                           w.head_dim, splits)),
-                         dtype=torch.uint8, device=dev)
-
-        def step():  # noqa: F811
-            fa.forward_splitk(q, k, v, causal=w.causal, sm_scale=w.sm_scale, layout=layout,
-                              num_splits=splits, out=o, lse=lse, workspace=ws)
-
+    st = Setup(args.workload, dev, splits=args.splits if args.which == "fwd" else 1)
+    w = st.w
     if args.which == "bwd":
-        return bench_bwd(args, w, inp, up, q, k, v, o, lse, layout, stream)
+        return bench_bwd(args, w, st.inp, lambda a: upload(w, a, dev), st.q, st.k, st.v, st.o,
+                         st.lse, st.layout, st.stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    region0 = torch.cuda.Event(enable_timing=True)
-    region1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    region0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    region1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_region = region0.elapsed_time(region1)
-    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    ms_avg = sum(per_launch) / len(per_launch)
-    ms_per_step = ms_region / args.steps
-    flops = w.flops()
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (ms_avg * 1e-3) / 1e12
+    ms_per_step, per_launch, t_wall = time_launches(st.step, st.stream, args.steps, args.warmup)
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (events), wall {t_wall:.3f} s, "
-          f"kernel avg {ms_avg:.4f} ms, median {per_launch[len(per_launch)//2]:.4f}, "
-          f"min {per_launch[0]:.4f}", file=sys.stderr, flush=True)
+          f"kernel avg {sum(per_launch) / len(per_launch):.4f} ms, "
+          f"median {per_launch[len(per_launch)//2]:.4f}, min {per_launch[0]:.4f}",
+          file=sys.stderr, flush=True)
 
     if args.copy_calib:
         n = 1 << 30
@@ -329,35 +459,17 @@ def main():
         print(f"[bench] copy calibration: 3 copies of {n} bytes", file=sys.stderr, flush=True)
         del src, dst
 
-    traffic = load_traffic() if args.workload == "c5" else None
-    out = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": w.name, "key_splits": splits, "batch": w.batch, "heads": w.heads,
-                   "seq_q": w.seq_q,
-                   "seq_k": w.seq_k, "head_dim": w.head_dim, "causal": w.causal,
-                   "sm_scale": w.sm_scale, "flops_per_step": flops},
-        "pct_of_peak": round(100.0 * value / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel_ms_avg": round(ms_avg, 5),
-                     "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
-                     "kernel_ms_min": round(per_launch[0], 5)},
-        "context": {"rtx3090_unfused_per_call": CONTEXT_RTX3090},
-    }
+    out = bench_line(w, args.workload, args.steps, args.warmup, st.splits, ms_per_step,
+                     per_launch, st.peak)
     if not args.no_cpu_baseline and args.workload == "c5":
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp)
+        base, rows, o_ref, lse_ref = cpu_baseline(st.inp)
+        out["cpu_baseline"] = base
+        # the timed run's output on the same rows (flat ids over [B*H*Sq])
+        o_g = to_bhsd_f64(st.o, st.layout).reshape(-1, w.head_dim)[rows]
+        l_g = st.lse.detach().double().cpu().numpy().reshape(-1)[rows]
+        out["parity"] = error_summary(o_g, l_g, o_ref, lse_ref, rows.size,
+                                      "fp64 C oracle on the cpu_baseline sample rows")
     print(json.dumps(out), flush=True)
     return 0
 

@@ -128,6 +128,12 @@ def test_bwd_c3_shape():
     full_bwd_parity(w)
 
 
+def test_bwd_c4_shape():
+    """bf16 [4,32,4096,80] causal: every gradient element against the oracle."""
+    w = synth.WORKLOADS["c4"]
+    full_bwd_parity(w)
+
+
 def test_bwd_shd_layout_distinct_head_strides():
     # [seq, heads, d] with seq_q != seq_k: the head strides of q and k differ
     w = synth.custom("bwd fp16 shd", "fp16", "shd", 1, 4, 300, 417, 64, sm_scale=0.5, seed=9)

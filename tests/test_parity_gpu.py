@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from tiled_attention_04_amd import synth
-from gpu_cases import full_parity, sampled_parity, sampled_rows, say, run_gpu, to_device
+from gpu_cases import (full_parity, sampled_parity, sampled_rows, say, run_gpu, to_device,
+                       whole_parity_chunked)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +30,16 @@ def _device():
 @pytest.mark.parametrize("key", ["c1", "c2", "c3"])
 def test_workload_full(key):
     full_parity(synth.make_inputs(key), name=key)
+
+
+def test_workload_c4_whole_output():
+    """Every row of C4 (bf16 [4,32,4096,80] causal) against the oracle."""
+    whole_parity_chunked(synth.make_inputs("c4"), name="c4", heads_per_chunk=16)
+
+
+def test_workload_c5_whole_output():
+    """Every row of C5 (bf16 [1,16,32768,128] causal, 1% of K rows x8)."""
+    whole_parity_chunked(synth.make_inputs("c5"), name="c5", heads_per_chunk=2)
 
 
 def test_workload_c4_sampled():
