@@ -161,6 +161,7 @@ def whole_parity_chunked(inp, name=None, heads_per_chunk=2, record=None):
     pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
     o_max = l_max = 0.0
     o_sum = l_sum = 0.0
+    worst = "-"
     t0 = time.time()
     for c in range(0, len(pairs), heads_per_chunk):
         chunk = pairs[c:c + heads_per_chunk]
@@ -172,6 +173,10 @@ def whole_parity_chunked(inp, name=None, heads_per_chunk=2, record=None):
         l_g = np.stack([lse_all[b, h] for (b, h) in chunk])[:, None]
         eo = np.abs(o_g - o_ref)
         el = np.abs(l_g - lse_ref)
+        if float(eo.max()) > o_max:
+            n, _, i, d = np.unravel_index(int(np.argmax(eo)), eo.shape)
+            worst = (f"(b, h) {chunk[n]} row {i} dim {d}: gpu {o_g[n, 0, i, d]:.6f} "
+                     f"oracle {o_ref[n, 0, i, d]:.6f}")
         o_max, o_sum = max(o_max, float(eo.max())), o_sum + float(eo.sum())
         l_max, l_sum = max(l_max, float(el.max())), l_sum + float(el.sum())
         say(f"  {name}: heads {c}..{c + len(chunk) - 1} of {len(pairs)} checked "
@@ -180,7 +185,7 @@ def whole_parity_chunked(inp, name=None, heads_per_chunk=2, record=None):
     l_mean = l_sum / lse_all.size
     tol = TOL[w.dtype]
     msg = (f"{name} (whole output): O max {o_max:.3e} mean {o_mean:.3e} | "
-           f"lse max {l_max:.3e} mean {l_mean:.3e}")
+           f"lse max {l_max:.3e} mean {l_mean:.3e}; largest O error at {worst}")
     say(msg)
     if record is not None:
         record.update(o_max_abs=o_max, o_mean_abs=o_mean, lse_max_abs=l_max, lse_mean_abs=l_mean,

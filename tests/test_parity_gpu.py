@@ -181,3 +181,42 @@ def test_repeat_is_bitwise_deterministic():
     o1, l1 = run_gpu(inp)
     o2, l2 = run_gpu(inp)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---- large grids at head_dim 97..128: the 64-row-per-wave kernel's domain ----
+
+LARGE_GRID = [
+    # (dtype, heads, seq_q, seq_k, head_dim, causal)
+    ("bf16", 1024, 200, 333, 128, False),   # one query tile per head, ragged keys
+    ("bf16", 1024, 200, 333, 128, True),
+    ("bf16", 512, 300, 129, 128, False),    # a ragged second query tile, 3 key tiles
+    ("bf16", 512, 300, 300, 128, True),
+    ("bf16", 256, 700, 1000, 120, True),    # head_dim padding inside the 128 slots
+    ("bf16", 1024, 64, 64, 104, False),     # one key tile
+    ("bf16", 1024, 17, 1, 112, False),      # a single key
+    ("fp16", 512, 300, 517, 128, True),
+    ("fp16", 256, 1000, 200, 128, False),
+]
+
+
+@pytest.mark.parametrize("dtype,heads,sq,sk,d,causal", LARGE_GRID)
+def test_large_grid_head_dim_128(dtype, heads, sq, sk, d, causal):
+    w = synth.custom("large grid", dtype, "bhsd", 1, heads, sq, sk, d, causal=causal,
+                     seed=600 + sq + sk + d)
+    full_parity(synth.make_inputs(w), name=f"large grid {dtype} h={heads} sq={sq} sk={sk} d={d} "
+                                           f"causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_large_grid_scales(scale):
+    w = synth.custom("large grid scale", "bf16", "bhsd", 2, 512, 256, 400, 128, causal=True,
+                     seed=650)
+    full_parity(synth.make_inputs(w), sm_scale=scale, name=f"large grid sm_scale={scale}")
+
+
+def test_large_grid_stress_rescales():
+    """Keys scaled x32 in a long causal row: the running maximum is raised
+    (and the accumulators rescaled) many times per row."""
+    w = synth.custom("large grid stress", "bf16", "bhsd", 1, 128, 2048, 2048, 128, causal=True,
+                     seed=651, stress_frac=0.03, stress_factor=32.0)
+    full_parity(synth.make_inputs(w), name="large grid stress x32")

@@ -127,6 +127,11 @@ struct Mfma<__bf16> {
     bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
     return __builtin_bit_cast(uint32_t, r);
   }
+  // acc + both halves of a packed pair, in fp32 (v_dot2_f32_bf16 against (1, 1))
+  __device__ static inline float sum2(uint32_t packed, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc, false);
+  }
 };
 
 template <>
@@ -139,6 +144,10 @@ struct Mfma<_Float16> {
     f32x2_t v = {x, y};
     f16x2_t r = __builtin_convertvector(v, f16x2_t);
     return __builtin_bit_cast(uint32_t, r);
+  }
+  __device__ static inline float sum2(uint32_t packed, float acc) {  // v_dot2_f32_f16
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), one, acc, false);
   }
 };
 
@@ -384,7 +393,12 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     }
   };
 
-  // P = exp2(s*c - m) rounded to the input type, and its partial row sum
+  // P = exp2(s*c - m) rounded to the input type, and its partial row sum.
+  // The sum is taken over the rounded weights, exactly the ones the P.V
+  // product consumes, so O = acc / l is a convex combination of V rows: with
+  // the unrounded sum, a row dominated by one key whose weight rounds off by
+  // 2^-9 carries that relative error into O (up to 0.01 at |O| ~ 6, on top of
+  // O's own bf16 rounding).
   auto probs = [&](const f32x16_t (&s)[2], uint32_t (&pk)[2][8]) {
     const float msub = (m_run == -INFINITY) ? 0.f : m_run;
     float part[4] = {0.f, 0.f, 0.f, 0.f};  // four short add chains instead of one long one
@@ -394,8 +408,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
         const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
-        part[(r >> 1) & 3] += p0 + p1;
         pk[kb2][r >> 1] = M::pack2(p0, p1);
+        part[(r >> 1) & 3] = M::sum2(pk[kb2][r >> 1], part[(r >> 1) & 3]);
       }
     l_run += (part[0] + part[1]) + (part[2] + part[3]);
   };
