@@ -17,10 +17,12 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    """Always recompiles; returns the path of the built library."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+def build(verbose=False, out=None, extra=()):
+    """Always recompiles; returns the path of the built library.  `out` and
+    `extra` build a variant (the tests' LDS race-check library)."""
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + list(extra) + SOURCES + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)
@@ -28,8 +30,8 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -283,6 +283,11 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
 
   // one key tile; its K / V are in stage kb, the next tile loads into nb
   auto step = [&](int t, FA_LDS char* kb, FA_LDS char* nb) {
+#ifdef FA_LDS_POISON
+    lds_poison<64 * NW>(nb, G::STAGE);  // tile t - 1 (read in the previous step) is free
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#endif
     if (t + 1 < n_tiles) issue(t + 1, nb);
     FA_LDS char* vb = kb + G::KBYTES;
 
@@ -529,6 +534,11 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   // one query tile; its Q / dO tile is in stage qb, the next tile loads
   // into the other stage nb meanwhile
   auto step = [&](int t, FA_LDS char* qb, FA_LDS char* nb) {
+#ifdef FA_LDS_POISON
+    lds_poison<64 * NW>(nb, G::STAGE);  // tile t - 1 (read in the previous step) is free
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#endif
     if (t + 1 < qt_end) {
       issue(t + 1, nb);
       stats_load(t + 1);

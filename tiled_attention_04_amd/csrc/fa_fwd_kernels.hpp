@@ -151,6 +151,18 @@ struct Mfma<_Float16> {
   }
 };
 
+#ifdef FA_LDS_POISON
+// Race check (a debug build only): the kernels fill an LDS area with NaN
+// (all-ones 16-bit words) once the barrier that ends its last read has
+// passed, just before its next tile is loaded; a wave that read a stage
+// outside its window would then see NaN, which the parity tests catch.
+template <int NT>
+__device__ inline void lds_poison(FA_LDS char* base, int bytes) {
+  for (int off = (int)threadIdx.x * 16; off < bytes; off += NT * 16)
+    *(FA_LDS u32x4_t*)(base + off) = (u32x4_t){0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+}
+#endif
+
 // Smallest row stride (bytes, multiple of 16, >= min_bytes) congruent to 64
 // or 192 modulo 256: then the 4 rows x 64 bytes that 32 lanes of a
 // transposing read gather fall into disjoint bank windows.
@@ -443,6 +455,14 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   using Odd = std::integral_constant<int, 1>;
   auto step = [&](int t, auto parity, auto has_next, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     constexpr int P = decltype(parity)::value;
+#ifdef FA_LDS_POISON
+    // K(t) (read by S(t) in the previous step) and V(t - 1) (read by P V in
+    // the previous step) are free now; K(t + 2) and V(t + 1) refill them
+    lds_poison<G::NT>(lds + P * G::STAGE, G::KBYTES);
+    lds_poison<G::NT>(lds + (1 - P) * G::STAGE + G::KBYTES, G::VBYTES);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#endif
     stats(t, cur);
     if (t + 2 < t1) issue_k(t + 2);
     if (t + 1 < t1) issue_v(t + 1);
