@@ -32,6 +32,8 @@ Other modes:
   --copy-calib          also run a plain device copy of 1 GiB (for counter
                         calibration under rocprofv3 --pmc)
   --summarize-pmc DIR   reduce rocprofv3 --pmc output under DIR to a summary
+  --write-traffic F W   profiles/traffic_<workload>.json from a FETCH_SIZE and a
+                        WRITE_SIZE rocprofv3 --pmc pass (with --copy-calib)
   --pass bwd            time the backward (fa_bwd: delta, dQ and dK/dV launches)
                         on the same workload instead; FLOPs counted as 2.5x the
                         forward's (the five products of the backward), so the
@@ -178,6 +180,36 @@ def summarize_pmc(d):
     for (k, c), (n, s) in sorted(out.items()):
         res.setdefault(k, {})[c] = {"mean": s / n, "samples": n}
     return res
+
+
+def write_traffic(key, fetch_dir, write_dir, command):
+    """profiles/traffic_<key>.json from two rocprofv3 --pmc passes (FETCH_SIZE,
+    then WRITE_SIZE) of `bench.py --copy-calib` runs: the forward kernel's
+    per-dispatch KiB, each scaled by what the same counter read for the plain
+    1 GiB device copy the run makes (its bytes over the counter's bytes)."""
+    fetch, write = summarize_pmc(fetch_dir), summarize_pmc(write_dir)
+
+    def pick(res, counter, needle):
+        hits = [(k, v[counter]["mean"]) for k, v in res.items() if needle in k and counter in v]
+        assert len(hits) == 1, (needle, [h[0] for h in hits])
+        return hits[0]
+    kname, f_kib = pick(fetch, "FETCH_SIZE", "fa_fwd")
+    _, w_kib = pick(write, "WRITE_SIZE", "fa_fwd")
+    _, f_copy = pick(fetch, "FETCH_SIZE", "copyBuffer")
+    _, w_copy = pick(write, "WRITE_SIZE", "copyBuffer")
+    n = 1 << 30
+    f_fac, w_fac = n / (f_copy * 1024), n / (w_copy * 1024)
+    out = {"kernel": kname, "workload_key": key, "kernel_source_hash": kernel_source_hash(),
+           "fetch_size_kib": f_kib, "write_size_kib": w_kib,
+           "copy_calibration": {"bytes_read_and_written": n, "fetch_size_kib": f_copy,
+                                "write_size_kib": w_copy, "fetch_factor": round(f_fac, 4),
+                                "write_factor": round(w_fac, 4)},
+           "hbm_bytes_per_launch": int(round(f_kib * 1024 * f_fac + w_kib * 1024 * w_fac)),
+           "command": command}
+    path = os.path.join(PROFILES, f"traffic_{key}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return path
 
 
 def bench_bwd(args, w, inp, up, q, k, v, o, lse, layout, stream):
@@ -411,6 +443,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--summarize-pmc", default=None)
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "output directories (FETCH_SIZE pass, WRITE_SIZE pass)")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     ap.add_argument("--splits", type=int, default=1,
                     help="forward through fa_fwd_splitk with this many key splits "
@@ -419,6 +454,12 @@ def main():
 
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
+        return 0
+    if args.write_traffic:
+        cmd = (f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
+               f"python -u bench.py --workload {args.workload} --no-cpu-baseline --steps 3 "
+               f"--warmup 1 --copy-calib")
+        print(write_traffic(args.workload, *args.write_traffic, cmd))
         return 0
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU; --gpus {args.gpus} is not "
