@@ -154,6 +154,33 @@ fa_status_t fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, 
                           fa_dtype_t dtype, int num_splits, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * fa_fwd_splitk_static -- fa_fwd_splitk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the fp32 split partials go to a fixed device array
+ * inside the library instead of a caller workspace.  Same arguments (minus
+ * workspace, workspace_bytes), semantics, layouts and validation as
+ * fa_fwd_splitk.  The call itself allocates nothing: no hipMalloc, hipFree
+ * or allocating library routine.
+ *
+ * The array holds FA_SPLITK_STATIC_MAX_BYTES bytes on every GPU the library
+ * runs on, for the life of the process; a call whose partials
+ * (fa_fwd_splitk_workspace(batch, heads, seq_q, head_dim, splits) bytes)
+ * would exceed it returns FA_ERR_WORKSPACE before any HIP call.  Its device
+ * address is looked up once per device (hipGetSymbolAddress, with that device
+ * current; a failure there returns FA_ERR_HIP).  Nothing in it needs to start
+ * at zero: every split writes all of its partial rows before the merge reads
+ * them.  All calls on one GPU share its array, so calls that overlap on that
+ * GPU (on different streams, or from different host threads without ordering)
+ * race; calls on one stream are ordered and safe.
+ */
+#define FA_SPLITK_STATIC_MAX_BYTES ((size_t)32 << 20)
+fa_status_t fa_fwd_splitk_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                                 int64_t head_dim, fa_strides_t q_st, fa_strides_t k_st,
+                                 fa_strides_t v_st, fa_strides_t o_st, float sm_scale, int causal,
+                                 fa_dtype_t dtype, int num_splits, void* stream);
+
 /* Number of key splits fa_fwd_splitk uses for num_splits == 0: about one
  * workgroup per CU, at least eight 64-key tiles per split, at most 16; 1
  * when the unsplit grid already has 256 workgroups.  Never fails (1 for empty

@@ -220,3 +220,33 @@ def test_bwd_rejects_key_launch_beyond_32bit_work_items():
                    sq, sk, sk, sq, sq, sq, sk, sk, 0.125, 0, BF16, None)
     assert rc == 2, (rc, fa.last_error())
     assert "work-items" in fa.last_error()
+
+
+def test_splitk_static_rejects_partials_beyond_its_array():
+    # 8 splits x 16 heads x 4096 rows x 129 floats = 270 MB > 32 MiB: refused before any HIP call
+    st = _contig(4096, 16, 128)
+    rc = fa.fa_fwd_splitk_static(P, P, P, P, None, 1, 16, 4096, 4096, 128, st, st, st, st, 0.125, 0,
+                                 BF16, 8, None)
+    assert rc == 8, (rc, fa.last_error())
+    assert "static scratch" in fa.last_error()
+    need = fa.fa_fwd_splitk_workspace(1, 16, 4096, 128, 8)
+    assert need > fa.SPLITK_STATIC_MAX_BYTES
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(batch=-1), 2), (dict(sk=0), 2), (dict(dtype=F32), 3), (dict(splits=17), 8),
+    (dict(q=None), 1), (dict(d=12), 4),
+])
+def test_splitk_static_validation_errors(kwargs, code):
+    args = dict(q=P, k=P, v=P, o=P, batch=1, heads=2, sq=128, sk=128, d=64, dtype=BF16, splits=2)
+    args.update(kwargs)
+    rc = fa.fa_fwd_splitk_static(args["q"], args["k"], args["v"], args["o"], None, args["batch"],
+                                 args["heads"], args["sq"], args["sk"], args["d"], CONTIG, CONTIG,
+                                 CONTIG, CONTIG, 0.125, 0, args["dtype"], args["splits"], None)
+    assert rc == code, (kwargs, rc, fa.last_error())
+
+
+def test_splitk_static_empty_problem_is_ok_without_pointers():
+    rc = fa.fa_fwd_splitk_static(None, None, None, None, None, 0, 2, 128, 128, 64, CONTIG, CONTIG,
+                                 CONTIG, CONTIG, 0.125, 0, BF16, 2, None)
+    assert rc == 0

@@ -21,7 +21,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_DTYPE",
           4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_LAYOUT", 6: "FA_ERR_HIP", 7: "FA_ERR_SCALE",
           8: "FA_ERR_WORKSPACE"}
 EXPORTS = ("fa_fwd", "fa_fwd_splitk", "fa_fwd_splitk_choose", "fa_fwd_splitk_workspace",
-           "fa_bwd", "fa_status_string", "fa_last_error", "fa_version")
+           "fa_fwd_splitk_static", "fa_bwd", "fa_status_string", "fa_last_error", "fa_version")
+SPLITK_STATIC_MAX_BYTES = 32 << 20  # FA_SPLITK_STATIC_MAX_BYTES of include/fa.h
 
 
 class FaStrides(ctypes.Structure):
@@ -55,6 +56,11 @@ def lib():
         L.fa_fwd_splitk.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [FaStrides] * 4 +
                                     [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+        L.fa_fwd_splitk_static.restype = ctypes.c_int
+        L.fa_fwd_splitk_static.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 +
+                                           [FaStrides] * 4 +
+                                           [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p])
         L.fa_fwd_splitk_choose.restype = ctypes.c_int
         L.fa_fwd_splitk_choose.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
         L.fa_fwd_splitk_workspace.restype = ctypes.c_size_t
@@ -87,6 +93,15 @@ def fa_fwd_splitk(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k
     return lib().fa_fwd_splitk(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, *st,
                                float(sm_scale), int(causal), int(dtype), int(num_splits),
                                workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_splitk_static(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_st,
+                         o_st, sm_scale, causal, dtype, num_splits, stream):
+    """Direct call of the C entry point; returns the integer status."""
+    st = [s if isinstance(s, FaStrides) else FaStrides(*s) for s in (q_st, k_st, v_st, o_st)]
+    return lib().fa_fwd_splitk_static(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, *st,
+                                      float(sm_scale), int(causal), int(dtype), int(num_splits),
+                                      stream)
 
 
 def fa_fwd_splitk_choose(batch, heads, seq_q, seq_k, head_dim, causal):

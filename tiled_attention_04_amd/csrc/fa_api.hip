@@ -6,12 +6,20 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernels.hpp"
 #include "fa_bwd_kernels.hpp"
 #include "fa_fp8_kernels.hpp"
+
+// Split partials of fa_fwd_splitk_static, for callers that cannot allocate:
+// a fixed device array per GPU (each GPU the library runs on holds its own
+// copy for the life of the process).  Host code never uses this name as an
+// address: the device address comes from hipGetSymbolAddress, per device.
+constexpr size_t kStaticScratchBytes = FA_SPLITK_STATIC_MAX_BYTES;
+__device__ __attribute__((aligned(256))) char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -325,12 +333,37 @@ fa_status_t launch_bwd_16bit(const fa::BwdArgs& a, int64_t head_dim, void* strea
 
 
 
-// Shared by fa_fwd (splits == 1, no workspace) and fa_fwd_splitk.
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fa_status_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_HIP, "device %d beyond the %d devices the static scratch serves", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+// Shared by fa_fwd (splits == 1, no workspace), fa_fwd_splitk and
+// fa_fwd_splitk_static (use_static: the partials go to `scratch`).
 fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
                      fa_strides_t q_st, fa_strides_t k_st, fa_strides_t v_st, fa_strides_t o_st,
                      float sm_scale, int causal, fa_dtype_t dtype, int splits, void* workspace,
-                     size_t workspace_bytes, bool split_api, void* stream) {
+                     size_t workspace_bytes, bool split_api, void* stream, bool use_static = false) {
   if (batch < 0 || heads < 0 || seq_q < 0)
     return fail(FA_ERR_SHAPE, "batch, heads and seq_q must be >= 0");
   if (seq_k < 1) return fail(FA_ERR_SHAPE, "seq_k must be >= 1 (softmax over no keys)");
@@ -383,7 +416,11 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     return fail(FA_ERR_LAYOUT, "q, k, v and o must be %d-byte aligned", (int)align);
   if (lse && !aligned(lse, 4)) return fail(FA_ERR_LAYOUT, "lse must be 4-byte aligned");
   const size_t need = splitk_workspace_bytes(batch * heads, seq_q, head_dim, splits);
-  if (need > 0) {
+  if (need > 0 && use_static) {
+    if (need > kStaticScratchBytes)
+      return fail(FA_ERR_WORKSPACE, "%zu bytes of split partials exceed the %zu-byte static scratch "
+                  "(fewer splits or fa_fwd_splitk with a workspace)", need, kStaticScratchBytes);
+  } else if (need > 0) {
     if (!workspace) return fail(FA_ERR_WORKSPACE, "a workspace of %zu bytes is needed", need);
     if (!aligned(workspace, 256)) return fail(FA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
@@ -406,13 +443,18 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   a.causal = causal ? 1 : 0;
   a.n_splits = splits;
   a.v_sd = v_st.dim;
-  if (splits > 1) {
+  if (splits > 1 && !use_static) {
     a.part_o = (float*)workspace;
     a.part_lse = a.part_o + (size_t)splits * (size_t)(batch * heads) * (size_t)seq_q * (size_t)head_dim;
   }
   // the merge runs after the split shares: bound its dispatch before any launch
   if (splits > 1) {
     if (fa_status_t s2 = check_dispatch((batch * heads * seq_q + 31) / 32, 256)) return s2;
+  }
+  if (need > 0 && use_static) {
+    if (fa_status_t s2 = static_scratch(&workspace)) return s2;
+    a.part_o = (float*)workspace;
+    a.part_lse = a.part_o + (size_t)splits * (size_t)(batch * heads) * (size_t)seq_q * (size_t)head_dim;
   }
   fa_status_t st;
   switch (dtype) {
@@ -463,6 +505,16 @@ fa_status_t fa_fwd_splitk(const void* q, const void* k, const void* v, void* o, 
   g_last_error.clear();
   return fwd_impl(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_st, o_st,
                   sm_scale, causal, dtype, num_splits, workspace, workspace_bytes, true, stream);
+}
+
+fa_status_t fa_fwd_splitk_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                                 int64_t head_dim, fa_strides_t q_st, fa_strides_t k_st,
+                                 fa_strides_t v_st, fa_strides_t o_st, float sm_scale, int causal,
+                                 fa_dtype_t dtype, int num_splits, void* stream) {
+  g_last_error.clear();
+  return fwd_impl(q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, q_st, k_st, v_st, o_st,
+                  sm_scale, causal, dtype, num_splits, nullptr, 0, true, stream, true);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
