@@ -6,6 +6,9 @@ Stage use, per kernel:
   forward (16-bit): step t reads K(t + 1) (stage (t + 1) & 1) and V(t)
     (stage t & 1); after the barrier that closes step t - 1, K(t) and
     V(t - 1) are free and receive K(t + 2) and V(t + 1);
+  forward, head_dim > 128: step t reads V(t) and K(t + 2) and, with three V
+    stages, V(t + 1); after the barrier that opens it, K(t + 1) and V(t - 1)
+    are free and receive K(t + 3) and V(t + 2) (three V stages) or V(t + 1);
   dQ: step t reads K/V tile t from one stage while tile t + 1 loads into the
     other, freed by the barrier that closed step t - 1;
   dK/dV: the same with Q/dO tiles (and their L, D values).
@@ -24,6 +27,7 @@ sys.path.insert(0, HERE)
 from tiled_attention_04_amd import synth  # noqa: E402
 from gpu_cases import full_parity  # noqa: E402
 import test_parity_bwd_gpu as bwd  # noqa: E402
+import test_parity_splitk_gpu as splitk  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 POISON_LIB = os.path.join(HERE, "libfa_lds_poison.so")
@@ -52,7 +56,9 @@ FWD = [
     ("fp16", "bhsd", 1, 4, 700, 1100, 128, False),   # many key tiles
     ("bf16", "bhsd", 4, 64, 512, 512, 128, True),    # 8-wave workgroups (large grid)
     ("bf16", "bhsd", 1, 2, 150, 190, 80, True),      # head_dim 80 (padded V blocks)
-    ("bf16", "bhsd", 1, 2, 150, 190, 256, True),     # head_dim 256 (two output passes)
+    ("bf16", "bhsd", 1, 2, 150, 190, 256, True),     # head_dim 256 (wide kernel, two V stages)
+    ("fp16", "bhsd", 1, 2, 300, 700, 192, False),    # head_dim 192 (wide kernel, three V stages)
+    ("bf16", "bhsd", 1, 3, 400, 900, 160, True),     # head_dim 160 (wide kernel, three V stages)
     ("fp16", "shd", 1, 800, 10, 4096, 32, False),    # the issue's 800-head case
 ]
 
@@ -63,6 +69,14 @@ def test_forward_with_poisoned_stages(dtype, layout, b, h, sq, sk, d, causal):
                      std=0.5 if dtype == "fp16" else 1.0, seed=700 + sq + d)
     full_parity(synth.make_inputs(w), name=f"poisoned LDS fwd {dtype} {layout} h={h} sq={sq} "
                                            f"sk={sk} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_splitk_with_poisoned_stages(d):
+    # key shares that start past the first tile (t0 > 0) and one-tile shares
+    w = synth.custom("lds race splitk", "bf16", "bhsd", 1, 3, 300, 900, d, causal=True,
+                     seed=790 + d)
+    splitk.splitk_parity(w, 5)
 
 
 def test_forward_c3_with_poisoned_stages():

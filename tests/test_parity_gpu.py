@@ -214,6 +214,35 @@ def test_large_grid_scales(scale):
     full_parity(synth.make_inputs(w), sm_scale=scale, name=f"large grid sm_scale={scale}")
 
 
+# ---- head_dim 193..256: the widest paddings, several key and query tiles ----
+
+HEAD_DIM_256 = [
+    # (dtype, heads, seq_q, seq_k, head_dim, causal)
+    ("bf16", 4, 300, 333, 256, True),
+    ("bf16", 4, 300, 333, 256, False),
+    ("fp16", 2, 129, 700, 248, True),      # head_dim padding inside the last block
+    ("bf16", 2, 1000, 64, 200, False),     # one key tile
+    ("bf16", 2, 1, 1, 256, False),         # a single query and key
+    ("fp16", 3, 700, 129, 256, True),      # causal with fewer keys than queries
+    ("bf16", 1, 513, 1025, 224, True),
+]
+
+
+@pytest.mark.parametrize("dtype,heads,sq,sk,d,causal", HEAD_DIM_256)
+def test_head_dim_256_tiles(dtype, heads, sq, sk, d, causal):
+    w = synth.custom("head_dim 256", dtype, "bhsd", 1, heads, sq, sk, d, causal=causal,
+                     seed=700 + sq + sk + d)
+    full_parity(synth.make_inputs(w), name=f"head_dim {d} {dtype} h={heads} sq={sq} sk={sk} "
+                                           f"causal={causal}")
+
+
+def test_head_dim_256_stress_rescales():
+    """head_dim 256 with keys scaled x32: many rescales of the 256-wide accumulator."""
+    w = synth.custom("head_dim 256 stress", "bf16", "bhsd", 1, 8, 1024, 1024, 256, causal=True,
+                     seed=760, stress_frac=0.03, stress_factor=32.0)
+    full_parity(synth.make_inputs(w), name="head_dim 256 stress x32")
+
+
 def test_large_grid_stress_rescales():
     """Keys scaled x32 in a long causal row: the running maximum is raised
     (and the accumulators rescaled) many times per row."""

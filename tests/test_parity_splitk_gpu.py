@@ -58,11 +58,19 @@ def test_splitk_explicit(dtype, causal, splits):
     splitk_parity(w, splits)
 
 
-@pytest.mark.parametrize("head_dim", [32, 80, 128, 256])
+@pytest.mark.parametrize("head_dim", [32, 80, 128, 144, 192, 200, 256])
 def test_splitk_head_dims(head_dim):
     w = synth.custom(f"splitk d{head_dim}", "bf16", "bhsd", 1, 4, 200, 1000, head_dim,
                      causal=True, seed=32)
     splitk_parity(w, 4)
+
+
+@pytest.mark.parametrize("dtype,causal,splits", [("fp16", False, 3), ("bf16", True, 16)])
+def test_splitk_head_dim_256_shares(dtype, causal, splits):
+    # head_dim 256 with ragged shares; 16 splits leave most causal shares empty
+    w = synth.custom("splitk d256 shares", dtype, "bhsd", 1, 3, 300, 650, 256, causal=causal,
+                     seed=34)
+    splitk_parity(w, splits)
 
 
 def test_splitk_more_splits_than_tiles():

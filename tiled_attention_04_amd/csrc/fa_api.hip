@@ -11,6 +11,7 @@
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernels.hpp"
+#include "fa_fwd_wide.hpp"
 #include "fa_bwd_kernels.hpp"
 #include "fa_fp8_kernels.hpp"
 
@@ -81,10 +82,18 @@ fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& 
 }
 
 // Instantiated head-dim paddings: the smallest one >= head_dim is used.
-template <typename T, int D, int NW, int OCC, int DV = D>
+template <typename T, int D, int NW, int OCC>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_16bit(fa::FwdArgs a) {
-  fa::fa_fwd_16bit_body<T, D, NW, DV>(a);
+  fa::fa_fwd_16bit_body<T, D, NW>(a);
+}
+
+// head_dim 129..256 in one pass: 4 waves of 32 query rows, one per SIMD, Q
+// and the O^T accumulator in AGPRs
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_fwd_wide(fa::FwdArgs a) {
+  fa::fa_fwd_wide_body<T, D>(a);
 }
 
 // Workgroups of 8 waves (256 query rows) halve the K/V traffic per query and
@@ -101,23 +110,14 @@ fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   if (head_dim <= DP) return launch(fa_fwd_16bit<T, DP, NW, OCC>, grid, 64 * NW, a, stream);
   FA_CASE(32) FA_CASE(64) FA_CASE(80) FA_CASE(96) FA_CASE(128)
 #undef FA_CASE
-  // head_dim > 128 does not fit two waves per SIMD: 4-wave workgroups, one wave per SIMD
-#define FA_CASE(DP)                                                            \
-  if (head_dim <= DP) return launch(fa_fwd_16bit<T, DP, 4, 1>, grid4, 256, a4, stream);
+  // head_dim > 128: the wide kernel, 4-wave workgroups (128 query rows)
   fa::FwdArgs a4 = a;
   a4.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
   const int64_t grid4 = (int64_t)a.n_bh * a4.n_qtiles * a.n_splits;
   if (grid4 > kInt32Max) return fail(FA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid4);
-  FA_CASE(160) FA_CASE(192)
-#undef FA_CASE
-  if (head_dim <= 256) {
-    // one pass at D = 256 spills registers: two passes, each contracting the
-    // scores over all dims and forming 128 of the output dims
-    const fa_status_t st = launch(fa_fwd_16bit<T, 256, 4, 1, 128>, grid4, 256, a4, stream);
-    if (st != FA_OK) return st;
-    a4.v_col0 = 128;
-    return launch(fa_fwd_16bit<T, 256, 4, 1, 128>, grid4, 256, a4, stream);
-  }
+  if (head_dim <= 160) return launch(fa_fwd_wide<T, 160>, grid4, 256, a4, stream);
+  if (head_dim <= 192) return launch(fa_fwd_wide<T, 192>, grid4, 256, a4, stream);
+  if (head_dim <= 256) return launch(fa_fwd_wide<T, 256>, grid4, 256, a4, stream);
   return fail(FA_ERR_HEAD_DIM, "head_dim %lld unsupported", (long long)head_dim);
 }
 

@@ -21,8 +21,8 @@
 //    directly the B operand of O^T += V^T P^T (keys permuted consistently on
 //    both operands); V^T fragments come from LDS with ds_read_b64_tr_b16,
 //    which transposes 4 keys x 16 dims per 16-lane group on the fly;
-//  * K/V tiles are double-buffered in LDS through registers (128-bit global
-//    loads issued one tile ahead), rows padded so the MFMA operand reads of
+//  * K/V tiles are double-buffered in LDS, loaded one tile ahead by buffer
+//    loads that write LDS directly, rows padded so the MFMA operand reads of
 //    one wave spread over the banks;
 //  * keys >= seq_k and (causal) keys > query are masked to -inf; key rows
 //    beyond seq_k and dims beyond head_dim are zero-filled;
@@ -33,7 +33,8 @@
 //    every tile;
 //  * workgroup ids are remapped so all query tiles of one (batch, head) run
 //    on the same XCD (shared L2 for its K/V stream), heaviest causal tiles
-//    first.
+//    first;
+//  * head_dim 129..256 runs the same method in fa_fwd_wide.hpp.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -85,9 +86,6 @@ struct FwdArgs {
   int32_t n_splits;   // 1: no splitting, O and lse written directly
   float* part_o;      // [n_splits, n_bh, seq_q, head_dim]
   float* part_lse;    // [n_splits, n_bh, seq_q]
-  // kernels that form only DV < D of the output dims: first V / O column of
-  // this launch (the scores always contract over the whole head_dim)
-  int32_t v_col0;
 };
 
 // Map the linear workgroup id to (batch*head, query tile, key split).
@@ -220,13 +218,13 @@ __device__ inline float row_max32(const f32x16_t& a, const f32x16_t& b) {
 // 16-bit inputs (bf16 / f16).  D = head_dim rounded up to 16, NW waves per
 // workgroup, OCC waves per SIMD targeted by the register allocator.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int DV = D>
+template <typename T, int D, int NW>
 struct Tile16 {
   static constexpr int BM = 32 * NW;           // query rows per workgroup
   static constexpr int BN = 64;                // keys per K/V tile
   static constexpr int NT = 64 * NW;           // threads per workgroup
   static constexpr int KSTEPS = D / 16;        // k-steps of the S^T MFMA (16 dims each)
-  static constexpr int DBLK = (DV + 31) / 32;  // 32-dim blocks of the O^T accumulator
+  static constexpr int DBLK = (D + 31) / 32;   // 32-dim blocks of the O^T accumulator
   // K rows: stride = 16 (mod 256) bytes, so the 32 lanes reading one 16-byte
   // chunk of 32 consecutive rows fall on distinct bank groups.
   static constexpr int KROW = D * 2 + 16;
@@ -243,16 +241,16 @@ struct Tile16 {
   static constexpr int VBYTES = BN * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int LDS_BYTES = 2 * STAGE;
-  static_assert(D % 16 == 0 && D <= 256, "head_dim padding");
+  static_assert(D % 16 == 0 && D <= 128, "head_dim padding (wider ones: fa_fwd_wide.hpp)");
   static_assert(KROW % 16 == 0 && VROW % 16 == 0, "16-byte aligned rows");
   static_assert((BN * KSLOTS) % 64 == 0 && (BN * VSLOTS) % 64 == 0, "whole wave loads");
 };
 
 // Body of the 16-bit kernel; the __global__ entry points that instantiate it
 // (with their occupancy attributes) are defined next to the launcher.
-template <typename T, int D, int NW, int DV = D>
+template <typename T, int D, int NW>
 __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
-  using G = Tile16<T, D, NW, DV>;
+  using G = Tile16<T, D, NW>;
   using M = Mfma<T>;
   typedef typename M::frag frag;
   constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
@@ -273,11 +271,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 
   const T* qg = (const T*)a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
   const T* kg = (const T*)a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
-  // output dims [vc0, vc0 + hd_v) of this launch (all of them unless DV < D)
-  const int vc0 = DV < D ? a.v_col0 : 0;
-  const int hd_v = DV < D ? min(DV, a.head_dim - vc0) : a.head_dim;
-  const T* vg = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh + vc0;
-  T* og = (T*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + vc0;
+  const T* vg = (const T*)a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  T* og = (T*)a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
 
   const int q0 = qt * G::BM;
   const int qw = q0 + wave * 32;        // first query row of this wave
@@ -322,7 +317,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   for (int n = 0; n < G::VPER; ++n) {
     const int slot = (wave + NW * n) * 64 + lane;
     const int row = slot / G::VSLOTS, ch = slot - (slot / G::VSLOTS) * G::VSLOTS;
-    voff[n] = ch * 8 < hd_v ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
+    voff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
   }
   // Tile j's K goes to the K area and its V to the V area of LDS stage j & 1;
   // rows >= seq_k and dims >= head_dim land as zeros.
@@ -340,7 +335,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   auto issue_v = [&](int j) {
     const int key0 = j * BN;
     const int rows = min(BN, a.seq_k - key0);
-    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + hd_v * 2);
+    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
     FA_LDS char* vb = lds + ((j - t0) & 1) * G::STAGE + G::KBYTES;
 #pragma unroll
     for (int n = 0; n < G::VPER; ++n)
@@ -513,20 +508,20 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = db * 32 + 8 * g + 4 * hi;
-        const uint32_t off = (d0 < hd_v && l32 < wave_rows)
-                                 ? (uint32_t)((l32 * a.head_dim + vc0 + d0) * 4) : kOutOfRange;
+        const uint32_t off = (d0 < a.head_dim && l32 < wave_rows)
+                                 ? (uint32_t)((l32 * a.head_dim + d0) * 4) : kOutOfRange;
         const u32x4_t w = {__float_as_uint(acc[db][4 * g + 0] * inv),
                            __float_as_uint(acc[db][4 * g + 1] * inv),
                            __float_as_uint(acc[db][4 * g + 2] * inv),
                            __float_as_uint(acc[db][4 * g + 3] * inv)};
         __builtin_amdgcn_raw_buffer_store_b128(w, rp, off, 0, 0);
       }
-    if (hi == 0 && l32 < wave_rows && vc0 == 0)
+    if (hi == 0 && l32 < wave_rows)
       a.part_lse[row0 + l32] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     return;
   }
   const float inv = 1.0f / l_tot;
-  const int32_t onrec = (wave_rows - 1) * (int32_t)a.o_ss * 2 + hd_v * 2;
+  const int32_t onrec = (wave_rows - 1) * (int32_t)a.o_ss * 2 + a.head_dim * 2;
   const auto ro = make_rsrc(og + (int64_t)qw * a.o_ss, onrec);
   const uint32_t orow = (uint32_t)(l32 * (int32_t)a.o_ss * 2);
 #pragma unroll
@@ -534,12 +529,12 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = db * 32 + 8 * g + 4 * hi;
-      const uint32_t off = (d0 < hd_v && l32 < wave_rows) ? orow + d0 * 2 : kOutOfRange;
+      const uint32_t off = (d0 < a.head_dim && l32 < wave_rows) ? orow + d0 * 2 : kOutOfRange;
       const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
                          M::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
       __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
     }
-  if (hi == 0 && a.lse != nullptr && my_q < a.seq_q && vc0 == 0)
+  if (hi == 0 && a.lse != nullptr && my_q < a.seq_q)
     a.lse[(int64_t)bh * a.seq_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
