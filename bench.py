@@ -27,6 +27,8 @@ Other modes:
                         short100 / short10 (few queries against 4096 keys) and
                         c5_e5m2 (the default workload in float8 e5m2, V passed
                         key-major; roofline against the dense fp8 MFMA peak)
+                        and hd256 (bf16 [1,16,8192,256] causal: the kernel of
+                        head_dim 129..256)
   --splits S            forward through fa_fwd_splitk with S key splits (0: the
                         library's choice)
   --copy-calib          also run a plain device copy of 1 GiB (for counter
@@ -439,7 +441,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c5",
-                    choices=["c1", "c2", "c3", "c4", "c5", "short100", "short10", "c5_e5m2"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "short100", "short10", "c5_e5m2",
+                             "hd256"])
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")

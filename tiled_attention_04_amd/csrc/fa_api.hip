@@ -93,8 +93,9 @@ void fa_fwd_16bit(fa::FwdArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_wide(fa::FwdArgs a) {
-  fa::fa_fwd_wide_body<T, D>(a);
+  fa::fa_fwd_wide_body<T, D, 4>(a);
 }
+
 
 // Workgroups of 8 waves (256 query rows) halve the K/V traffic per query and
 // run two waves per SIMD from one workgroup; 4-wave workgroups (128 rows) are

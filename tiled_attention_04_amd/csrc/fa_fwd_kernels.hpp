@@ -125,6 +125,7 @@ struct Mfma<__bf16> {
     bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
     return __builtin_bit_cast(uint32_t, r);
   }
+  static constexpr uint32_t kOneBits = 0x3F80u;  // 1.0
   // acc + both halves of a packed pair, in fp32 (v_dot2_f32_bf16 against (1, 1))
   __device__ static inline float sum2(uint32_t packed, float acc) {
     const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -143,6 +144,7 @@ struct Mfma<_Float16> {
     f16x2_t r = __builtin_convertvector(v, f16x2_t);
     return __builtin_bit_cast(uint32_t, r);
   }
+  static constexpr uint32_t kOneBits = 0x3C00u;  // 1.0
   __device__ static inline float sum2(uint32_t packed, float acc) {  // v_dot2_f32_f16
     const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), one, acc, false);
@@ -255,6 +257,13 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   typedef typename M::frag frag;
   constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
   constexpr int KROW = G::KROW, VROW = G::VROW;
+  // Row sum by the matrix core where the P.V product pads the head dims (D
+  // not a multiple of 32): V's column D is 1.0 in both LDS stages, so row D
+  // of O^T accumulates the sum of the rounded weights of each query along
+  // with the output, and the VALU row sum (16 dot products per tile and
+  // wave) and its rescale drop out.  The padding columns are written once
+  // and never loaded over.
+  constexpr bool kOnesCol = (D % 32) != 0;
 
   __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
   FA_LDS char* lds = (FA_LDS char*)smem;
@@ -307,6 +316,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 
   // ---- per-lane byte offsets of the direct-to-LDS tile loads (tile independent)
   uint32_t koff[G::KPER], voff[G::VPER];
+  bool vlive[G::VPER];  // (ones-column layout) this lane's V chunk lies below dim D
 #pragma unroll
   for (int n = 0; n < G::KPER; ++n) {
     const int slot = (wave + NW * n) * 64 + lane;
@@ -318,6 +328,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     const int slot = (wave + NW * n) * 64 + lane;
     const int row = slot / G::VSLOTS, ch = slot - (slot / G::VSLOTS) * G::VSLOTS;
     voff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
+    vlive[n] = ch * 8 < D;
   }
   // Tile j's K goes to the K area and its V to the V area of LDS stage j & 1;
   // rows >= seq_k and dims >= head_dim land as zeros.
@@ -339,17 +350,33 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     FA_LDS char* vb = lds + ((j - t0) & 1) * G::STAGE + G::KBYTES;
 #pragma unroll
     for (int n = 0; n < G::VPER; ++n)
-      if (wave + NW * n < G::VINSTR)
+      if (wave + NW * n < G::VINSTR && (!kOnesCol || vlive[n]))
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(vb + (wave + NW * n) * 1024), 16,
                                                  voff[n], 0, 0, 0);
   };
+  // (ones-column layout) V columns D..32 DBLK - 1 of both stages: 1.0 in
+  // column D, zeros after it; written once, never loaded over
+  auto pad_cols = [&](int stage) {
+    if constexpr (kOnesCol) {
+      constexpr int C0 = D / 8, NC = 4 * DBLK - D / 8;  // first padding chunk, padding chunks per row
+      for (int i = tid; i < BN * NC; i += G::NT) {
+        const int row = i / NC, chk = C0 + i % NC;
+        const u32x4_t val = {chk == C0 ? M::kOneBits : 0u, 0u, 0u, 0u};
+        *(FA_LDS u32x4_t*)(lds + stage * G::STAGE + G::KBYTES + row * VROW + chk * 16) = val;
+      }
+    }
+  };
+  if constexpr (kOnesCol) {
+    pad_cols(0);
+    pad_cols(1);
+  }
 
   // ---- online-softmax state (per lane: query l32; both halves agree on m)
   f32x16_t acc[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) acc[db] = (f32x16_t){};
   float m_run = -INFINITY;  // reference max, base-2 scaled units
-  float l_run = 0.f;        // partial row sum over this lane's keys
+  float l_run = 0.f;        // partial row sum over this lane's keys (not with the ones column)
   const float c = a.c;
 
   // lane-constant LDS offsets of the MFMA operand reads
@@ -393,7 +420,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     const bool upd = m_new > m_run + kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(upd)) {
       const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
-      l_run *= alpha;
+      if constexpr (!kOnesCol) l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
       m_run = upd ? m_new : m_run;
@@ -416,9 +443,9 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
         const float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -msub));
         const float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -msub));
         pk[kb2][r >> 1] = M::pack2(p0, p1);
-        part[(r >> 1) & 3] = M::sum2(pk[kb2][r >> 1], part[(r >> 1) & 3]);
+        if constexpr (!kOnesCol) part[(r >> 1) & 3] = M::sum2(pk[kb2][r >> 1], part[(r >> 1) & 3]);
       }
-    l_run += (part[0] + part[1]) + (part[2] + part[3]);
+    if constexpr (!kOnesCol) l_run += (part[0] + part[1]) + (part[2] + part[3]);
   };
 
   // O^T += V^T P^T with the V tile in stage P: four 16-key steps per 32-dim block
@@ -455,6 +482,11 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     // the previous step) are free now; K(t + 2) and V(t + 1) refill them
     lds_poison<G::NT>(lds + P * G::STAGE, G::KBYTES);
     lds_poison<G::NT>(lds + (1 - P) * G::STAGE + G::KBYTES, G::VBYTES);
+    if constexpr (kOnesCol) {  // the padding columns are never reloaded: restore them
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      pad_cols(1 - P);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #endif
@@ -495,7 +527,14 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
   if (!wave_live) return;
-  const float l_tot = xlane_sum(l_run);
+  float l_tot;
+  if constexpr (kOnesCol) {
+    // row D of O^T: local dim ld of the last block, held by the lanes of half h1
+    constexpr int ld = D - 32 * (DBLK - 1), r1 = 4 * (ld / 8) + ld % 4, h1 = (ld % 8) / 4;
+    l_tot = xlane_sum(hi == h1 ? acc[DBLK - 1][r1] : 0.f);
+  } else {
+    l_tot = xlane_sum(l_run);
+  }
   if (a.n_splits > 1) {
     // fp32 partials of this key share; a row that saw none of its keys has
     // l = 0 and gets O_r = 0, lse_r = -inf (weight 0 in the merge)

@@ -16,7 +16,7 @@
 //    fragments no longer fit beside them.  Here the MFMAs are inline
 //    assembly with fixed register classes, so Q and the accumulator live in
 //    AGPRs (only the matrix core reads them) and everything else in VGPRs:
-//    one wave per SIMD, no spills, one pass over the keys;
+//    one wave per SIMD (NW = 4), no spills, one pass over the keys;
 //  * the step is software-pipelined over three tiles so that all of a wave's
 //    matrix work of one step overlaps all of its softmax work: step t issues
 //      P(t) V(t)                (MFMAs, V^T by transposing reads)
@@ -24,20 +24,24 @@
 //      S(t + 2) = K(t + 2) Q^T  (MFMAs, K by 128-bit reads)
 //    with no dependence between the three parts, in an instruction order
 //    fixed by hand: one MFMA per slot, each followed by a short unit of the
-//    softmax.  A single wave per SIMD issues at most one instruction per
-//    cycle group, so the VALU work has to sit in the MFMA shadows rather than
-//    on a second wave; at this width each step carries enough MFMAs for it.
-//    The rescale of the accumulator that softmax(t + 1) may ask for is
-//    applied at the start of step t + 1, after P(t) V(t) is in;
-//  * K has two LDS stages, V three where they fit (D <= 192: the first V^T
-//    fragments of step t + 1 are read before the barrier that opens it),
-//    else two.  Tiles are loaded direct-to-LDS, K(t + 3) and V(t + 2) (three
-//    V stages) or V(t + 1) (two) during step t;
+//    softmax.  With one wave per SIMD the VALU work has to sit in the shadows
+//    of the wave's own MFMAs; above head_dim 128 each step carries enough
+//    MFMAs for it.  The rescale of the accumulator that softmax(t + 1) may
+//    ask for is applied at the start of step t + 1, after P(t) V(t) is in;
+//  * K and V have two LDS stages each, filled direct-to-LDS: K(t + 3) and
+//    V(t + 1) are loaded during step t.  The stage of every access is a
+//    compile-time parity, so the compiler can tell the stages apart and
+//    never makes a read wait for the loads into the other stage;
 //  * every step is a full one: near the end of the workgroup's key range the
 //    softmax of tile t + 1 >= t1 and the scores of tile t + 2 >= t1 run on
 //    tiles that are not part of it; the mask hides all of their keys from
 //    every row, so they change neither m, l nor the accumulator (one step
 //    body, one register allocation).
+//
+// The body also compiles for head_dim <= 128 with eight waves (two per
+// SIMD); there it is slower than the compiler-scheduled 32-row kernel, whose
+// softmax VALU work per MFMA is the larger share, so only the wide
+// instantiations are used.
 #pragma once
 #include "fa_fwd_kernels.hpp"
 
@@ -56,9 +60,11 @@ struct MfmaPin;
 template <>
 struct MfmaPin<__bf16> {
   typedef bf16x8_t frag;
-  // s = k q (no accumulator input); s must not overlap the sources
+  // s = k q (no accumulator input); s must not overlap the sources.  The two
+  // wait states keep a VALU write of a register of s just before apart from
+  // the MFMA's write of it.
   __device__ static inline void first(f32x16_t& s, const frag& k, const frag& q) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
   }
   __device__ static inline void next(f32x16_t& s, const frag& k, const frag& q) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "a"(q));
@@ -72,7 +78,7 @@ template <>
 struct MfmaPin<_Float16> {
   typedef f16x8_t frag;
   __device__ static inline void first(f32x16_t& s, const frag& k, const frag& q) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "a"(q));
   }
   __device__ static inline void next(f32x16_t& s, const frag& k, const frag& q) {
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "a"(q));
@@ -121,32 +127,31 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW_>
 struct TileWide {
-  static constexpr int NW = 4;            // waves per workgroup, one per SIMD
+  static constexpr int NW = NW_;          // waves per workgroup
   static constexpr int NT = 64 * NW;      // threads per workgroup
   static constexpr int BM = 32 * NW;      // query rows per workgroup
   static constexpr int BN = 64;           // keys per tile
   static constexpr int KSTEPS = D / 16;   // k-steps of S^T (16 dims each)
-  static constexpr int DBLK = D / 32;     // 32-dim blocks of O^T
+  static constexpr int DBLK = (D + 31) / 32;  // 32-dim blocks of O^T
   static constexpr int KROW = D * 2 + 16;                  // bytes, = 16 mod 256
   static constexpr int VROW = tr_row_stride(DBLK * 64);    // bytes, 64 or 192 mod 256
   static constexpr int KSLOTS = KROW / 16, VSLOTS = VROW / 16;
   static constexpr int KINSTR = BN * KSLOTS / 64, VINSTR = BN * VSLOTS / 64;
   static constexpr int KPER = (KINSTR + NW - 1) / NW, VPER = (VINSTR + NW - 1) / NW;
   static constexpr int KBYTES = BN * KROW, VBYTES = BN * VROW;
-  static constexpr int VST = 2 * KBYTES + 3 * VBYTES <= 160 * 1024 ? 3 : 2;
-  static_assert(D % 32 == 0 && D > 128 && D <= 256, "head_dim padding of the wide kernel");
+  static_assert(D % 16 == 0 && D <= 256, "head_dim padding of the wide kernel");
   static_assert((BN * KSLOTS) % 64 == 0 && (BN * VSLOTS) % 64 == 0, "whole wave loads");
 };
 
-template <typename T, int D>
+template <typename T, int D, int NW_>
 __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
-  using G = TileWide<T, D>;
+  using G = TileWide<T, D, NW_>;
   using M = Mfma<T>;
   using X = MfmaPin<T>;
   typedef typename M::frag frag;
-  constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK, NW = G::NW, VST = G::VST;
+  constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK, NW = G::NW;
   constexpr int KROW = G::KROW, VROW = G::VROW;
   constexpr int NPV = 4 * DBLK;     // P.V MFMAs per step (four 16-key steps per 32-dim block)
   constexpr int NS = 2 * KSTEPS;    // S MFMAs per step (two 32-key blocks)
@@ -157,13 +162,19 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
   __shared__ __attribute__((aligned(1024))) char k_st1[G::KBYTES];
   __shared__ __attribute__((aligned(1024))) char v_st0[G::VBYTES];
   __shared__ __attribute__((aligned(1024))) char v_st1[G::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char v_st2[VST == 3 ? G::VBYTES : 16];
-  FA_LDS char* const kst[2] = {(FA_LDS char*)k_st0, (FA_LDS char*)k_st1};
-  // V(j) lives in stage j % VST
-  auto vstage = [&](int j) -> FA_LDS char* {
-    const int r = j % VST;
-    return r == 0 ? (FA_LDS char*)v_st0 : r == 1 ? (FA_LDS char*)v_st1 : (FA_LDS char*)v_st2;
+  // K(j) and V(j) live in stage (j - t0) % 2.  Stages are picked by
+  // compile-time parities only: the compiler then knows which object a read
+  // touches and does not wait for the direct-to-LDS loads into the other.
+  auto kstage = [&](auto pc) -> FA_LDS char* {
+    if constexpr (decltype(pc)::value % 2 == 0) return (FA_LDS char*)k_st0;
+    else return (FA_LDS char*)k_st1;
   };
+  auto vstage = [&](auto pc) -> FA_LDS char* {
+    if constexpr (decltype(pc)::value % 2 == 0) return (FA_LDS char*)v_st0;
+    else return (FA_LDS char*)v_st1;
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -311,7 +322,6 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
 
   // operand fragments in flight ahead of their MFMAs (slots)
   constexpr int PDV = 3, PDK = 3;
-  frag vpre[PDV];  // first V^T fragments of the next step, read before its barrier (three V stages)
 
   // One step t (stage parity P = (t - t0) & 1 known at compile time).  On
   // entry: P(t) in pk_c, S(t + 1) in s_c; on exit P(t + 1) in pk_n and
@@ -324,11 +334,11 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
   // subtract, exp2 of the first" and "exp2 of the second, then round, pack
   // and sum the previous pair" -- and a last unit that packs pair 15.
   // Operand fragments are read from LDS PDV / PDK slots ahead of their MFMAs.
-  using Even = std::integral_constant<int, 0>;
-  using Odd = std::integral_constant<int, 1>;
   auto step = [&](int t, auto parity, f32x16_t (&s_c)[2], f32x16_t (&s_n)[2],
                   uint32_t (&pk_c)[2][8], uint32_t (&pk_n)[2][8]) {
     constexpr int P = decltype(parity)::value;
+    using Cur = std::integral_constant<int, P>;
+    using Nxt = std::integral_constant<int, 1 - P>;
     // S(t + 1) was last written by MFMAs: drain them before the VALU reads below
     mfma_drain_v(s_c[0], s_c[1]);
     // the rescale that softmax(t) asked for, now that P(t - 1) V(t - 1) is in
@@ -344,19 +354,19 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
       alpha = 1.f;
       mfma_drain_a<DBLK>(acc);  // VALU writes before the next MFMA reads them
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t + 2) and V(t + VST - 2) loads have landed
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t + 2) and V(t) loads have landed
     __syncthreads();                // ... everyone's; and K(t + 1), V(t - 1) are free
 #ifdef FA_LDS_POISON
-    lds_poison<G::NT>(kst[1 - P], G::KBYTES);
-    lds_poison<G::NT>(vstage(t + VST - 1), G::VBYTES);
+    lds_poison<G::NT>(kstage(Nxt{}), G::KBYTES);
+    lds_poison<G::NT>(vstage(Nxt{}), G::VBYTES);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #endif
-    if (t + 3 < t1) issue_k(t + 3, kst[1 - P]);
-    if (t + VST - 1 < t1) issue_v(t + VST - 1, vstage(t + VST - 1));
+    if (t + 3 < t1) issue_k(t + 3, kstage(Nxt{}));
+    if (t + 1 < t1) issue_v(t + 1, vstage(Nxt{}));
     mask(t + 1, s_c);
-    FA_LDS char* const vb = vstage(t);
-    FA_LDS char* const kb = kst[P];
+    FA_LDS char* const vb = vstage(Cur{});
+    FA_LDS char* const kb = kstage(Cur{});
 
     float mt[11];                  // partial maxima of the tree
     float msub = 0.f;
@@ -450,14 +460,9 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
     using Seg0 = std::integral_constant<int, 0>;
     using Seg1 = std::integral_constant<int, 1>;
 
-    // ---- P(t) V(t): slot j = V^T fragment j; with three V stages the first
-    // PDV fragments were read at the end of the previous step
+    // ---- P(t) V(t): slot j = V^T fragment j
     frag vq[NPV], kq[NS];
-    if constexpr (VST == 3) {
-      static_for<0, PDV>([&](auto mc) { vq[decltype(mc)::value] = vpre[decltype(mc)::value]; });
-    } else {
-      static_for<0, PDV>([&](auto mc) { vq[decltype(mc)::value] = v_frag(vb, decltype(mc)::value); });
-    }
+    static_for<0, PDV>([&](auto mc) { vq[decltype(mc)::value] = v_frag(vb, decltype(mc)::value); });
     static_for<0, NPV>([&](auto jc) {
       constexpr int j = decltype(jc)::value, u = j / DBLK, db = j % DBLK;
       if constexpr (j + PDV < NPV) vq[j + PDV] = v_frag(vb, j + PDV);
@@ -476,12 +481,6 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
       units_at(jc, Seg1{});
       __builtin_amdgcn_sched_barrier(0);
     });
-    // the first V^T fragments of the next step (V(t + 1) is complete since
-    // this step's barrier); after the last tile they are read but never used
-    if constexpr (VST == 3) {
-      FA_LDS char* const vn = vstage(t + 1);
-      static_for<0, PDV>([&](auto mc) { vpre[decltype(mc)::value] = v_frag(vn, decltype(mc)::value); });
-    }
     l += (part[0] + part[1]) + (part[2] + part[3]);
   };
 
@@ -489,13 +488,12 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
     // ---- prologue: S(t0) -> P(t0), and S(t0 + 1)
     f32x16_t s0[2], s1[2];
     uint32_t p0[2][8], p1[2][8];
-    issue_k(t0, kst[0]);
-    issue_v(t0, vstage(t0));
-    if (t0 + 1 < t1) issue_k(t0 + 1, kst[1]);
-    if (VST == 3 && t0 + 1 < t1) issue_v(t0 + 1, vstage(t0 + 1));
+    issue_k(t0, kstage(Even{}));
+    issue_v(t0, vstage(Even{}));
+    if (t0 + 1 < t1) issue_k(t0 + 1, kstage(Odd{}));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    scores(kst[0], s0);
+    scores(kstage(Even{}), s0);
     mfma_drain_v(s0[0], s0[1]);
     mask(t0, s0);
     {
@@ -514,16 +512,14 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
         }
       l = (part[0] + part[1]) + (part[2] + part[3]);
     }
-    scores(kst[1], s1);  // S(t0 + 1), masked whole later if t0 + 1 >= t1
-    __syncthreads();     // K(t0) consumed by all waves before K(t0 + 2) is loaded over it
+    scores(kstage(Odd{}), s1);  // S(t0 + 1), masked whole later if t0 + 1 >= t1
+    __syncthreads();            // K(t0) consumed by all waves before K(t0 + 2) is loaded over it
 #ifdef FA_LDS_POISON
-    lds_poison<G::NT>(kst[0], G::KBYTES);
+    lds_poison<G::NT>(kstage(Even{}), G::KBYTES);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #endif
-    if (t0 + 2 < t1) issue_k(t0 + 2, kst[0]);
-    if constexpr (VST == 3)
-      static_for<0, PDV>([&](auto mc) { vpre[decltype(mc)::value] = v_frag(vstage(t0), decltype(mc)::value); });
+    if (t0 + 2 < t1) issue_k(t0 + 2, kstage(Even{}));
 
     // ---- every step a full one; even steps read S from set 1 and write set 0
     for (int t = t0;; t += 2) {

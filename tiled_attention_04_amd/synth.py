@@ -94,6 +94,11 @@ EXTRA_WORKLOADS = {
     "c5_e5m2": Workload("e5m2 [1,16,32768,128] causal, 1% of K rows x8", "e5m2", "bhsd", 1, 16,
                         32768, 32768, 128, 1.0, 1.0 / math.sqrt(128.0), True, seed=25,
                         stress_frac=0.01, stress_factor=8.0),
+    # the widest head_dim of the forward (its one-pass kernel), long causal
+    # rows with the same key stress as the 32768-token workload
+    "hd256": Workload("bf16 [1,16,8192,256] causal, 1% of K rows x8", "bf16", "bhsd", 1, 16,
+                      8192, 8192, 256, 1.0, 1.0 / 16.0, True, seed=26,
+                      stress_frac=0.01, stress_factor=8.0),
 }
 
 _CHUNK = 1 << 22
