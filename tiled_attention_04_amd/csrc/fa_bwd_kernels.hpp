@@ -38,6 +38,7 @@
 //    (causal, key tail) or a query does not exist.
 #pragma once
 #include "fa_fwd_kernels.hpp"
+#include "fa_mfma_asm.hpp"
 
 namespace fa {
 
@@ -182,8 +183,14 @@ template <typename T, int D, int NW>
 __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
   using G = BwdQTile<T, D, NW>;
   using M = Mfma<T>;
+  using X = MfmaPin<T>;
   typedef typename M::frag frag;
   constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK, KR = G::KR, VR = G::VR;
+  // Above head_dim 128 the MFMAs are inline assembly that keeps the Q
+  // fragments and the dQ^T accumulator in AGPRs (4 DBLK + KSTEPS * 4
+  // registers, 192 at D = 256), where the register allocator would move them
+  // between AGPRs and VGPRs inside the key loop.
+  constexpr bool kPinAcc = D > 128;
 
   // the two tile stages as separate LDS objects, so that the compiler can
   // tell reads of one stage from the asynchronous loads into the other
@@ -232,6 +239,7 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
       dof[st] = __builtin_bit_cast(frag, rawd);
     }
   }
+  if constexpr (kPinAcc) pin_agpr<KSTEPS>(qf);
   const bool q_ok = my_q < a.seq_q;
   const float L2 = q_ok ? a.lse[(int64_t)bh * a.seq_q + my_q] * kLog2e : 0.f;
   const float Dl = q_ok ? a.delta[(int64_t)bh * a.seq_q + my_q] : 0.f;
@@ -293,21 +301,55 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
 
     // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks of the tile
     f32x16_t s[2], dp[2];
+    if constexpr (kPinAcc) {
+      // fragments read PD k-steps ahead of their MFMAs, scheduling barriers
+      // between the k-steps (bounded registers in flight)
+      constexpr int PD = 2;
+      frag kfr[KSTEPS][2], vfr[KSTEPS][2];
+      auto rd = [&](auto ic) {
+        constexpr int st = decltype(ic)::value;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s[kb2] = (f32x16_t){};
-      dp[kb2] = (f32x16_t){};
-    }
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          kfr[st][kb2] = __builtin_bit_cast(
+              frag, *(FA_LDS u32x4_t*)(kb + ((st & 1) ? k_odd : k_even) + kb2 * 32 * KR + 64 * (st >> 1)));
+          vfr[st][kb2] = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(vb + v_lane + kb2 * 32 * VR + st * 32));
+        }
+      };
+      static_for<0, PD>(rd);
+      static_for<0, KSTEPS>([&](auto ic) {
+        constexpr int st = decltype(ic)::value;
+        if constexpr (st + PD < KSTEPS) rd(std::integral_constant<int, st + PD>{});
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          if constexpr (st == 0) {
+            X::first(s[kb2], kfr[st][kb2], qf[st]);
+            X::vfirst(dp[kb2], vfr[st][kb2], dof[st]);
+          } else {
+            X::next(s[kb2], kfr[st][kb2], qf[st]);
+            X::vnext(dp[kb2], vfr[st][kb2], dof[st]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      mfma_drain_v(s[0], s[1]);  // before the VALU reads of S and dP
+      mfma_drain_v(dp[0], dp[1]);
+    } else {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const frag kf = __builtin_bit_cast(
-            frag, *(FA_LDS u32x4_t*)(kb + ((st & 1) ? k_odd : k_even) + kb2 * 32 * KR + 64 * (st >> 1)));
-        const frag vf = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(vb + v_lane + kb2 * 32 * VR + st * 32));
-        s[kb2] = M::mma(kf, qf[st], s[kb2]);
-        dp[kb2] = M::mma(vf, dof[st], dp[kb2]);
+        s[kb2] = (f32x16_t){};
+        dp[kb2] = (f32x16_t){};
       }
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const frag kf = __builtin_bit_cast(
+              frag, *(FA_LDS u32x4_t*)(kb + ((st & 1) ? k_odd : k_even) + kb2 * 32 * KR + 64 * (st >> 1)));
+          const frag vf = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(vb + v_lane + kb2 * 32 * VR + st * 32));
+          s[kb2] = M::mma(kf, qf[st], s[kb2]);
+          dp[kb2] = M::mma(vf, dof[st], dp[kb2]);
+        }
+    }
 
     // P = exp2(s c - L2) (0 where masked), dS = P (dP - D), rounded pairwise
     const int key0 = t * BN;
@@ -328,19 +370,36 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
       }
 
     // dQ^T += K^T dS^T: four 16-key steps per 32-dim block
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    auto ktr = [&](int u, int db) {
+      FA_LDS char* p0 = kb + (16 * u) * KR + db * 64;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + t_lo));
+      const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + t_up));
+      const u32x4_t kraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                            __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
+      return __builtin_bit_cast(frag, kraw);
+    };
+    auto s_frag = [&](int u) {
       const u32x4_t sraw = {pk[u >> 1][4 * (u & 1) + 0], pk[u >> 1][4 * (u & 1) + 1],
                             pk[u >> 1][4 * (u & 1) + 2], pk[u >> 1][4 * (u & 1) + 3]};
-      const frag sf = __builtin_bit_cast(frag, sraw);
+      return __builtin_bit_cast(frag, sraw);
+    };
+    if constexpr (kPinAcc) {
+      // the transposing reads PD blocks ahead of their MFMAs
+      constexpr int PD = 2, NB = 4 * DBLK;
+      frag kt[NB];
+      static_for<0, PD>([&](auto ic) { kt[decltype(ic)::value] = ktr(decltype(ic)::value / DBLK, decltype(ic)::value % DBLK); });
+      static_for<0, NB>([&](auto ic) {
+        constexpr int j = decltype(ic)::value, u = j / DBLK, db = j % DBLK;
+        if constexpr (j + PD < NB) kt[j + PD] = ktr((j + PD) / DBLK, (j + PD) % DBLK);
+        X::acc_fresh(acc[db], kt[j], s_frag(u));
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        FA_LDS char* p0 = kb + (16 * u) * KR + db * 64;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + t_lo));
-        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + t_up));
-        const u32x4_t kraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                              __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
-        acc[db] = M::mma(__builtin_bit_cast(frag, kraw), sf, acc[db]);
+      for (int u = 0; u < 4; ++u) {
+        const frag sf = s_frag(u);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) acc[db] = M::mma(ktr(u, db), sf, acc[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
@@ -360,6 +419,7 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
   }
 
   // dQ = scale * (K^T dS^T)^T, rounded to the input type
+  if constexpr (kPinAcc) mfma_drain_a<DBLK>(acc);  // the last MFMAs before the VALU reads
   if (wave_rows == 0) return;
   const int32_t onrec = (wave_rows - 1) * (int32_t)a.dq_ss * 2 + a.head_dim * 2;
   const auto ro = make_rsrc(dqg + (int64_t)qw * a.dq_ss, onrec);
@@ -409,8 +469,14 @@ template <typename T, int D, int NW>
 __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   using G = BwdKVTile<T, D, NW>;
   using M = Mfma<T>;
+  using X = MfmaPin<T>;
   typedef typename M::frag frag;
   constexpr int BQ = G::BQ, KSTEPS = G::KSTEPS, DBLK = G::DBLK, QR = G::QR;
+  // Above head_dim 128 the two accumulators take 2 x 4 DBLK registers (256
+  // at D = 256): their MFMAs are then written as inline assembly that keeps
+  // them in AGPRs, where the register allocator would shuttle them between
+  // AGPRs and VGPRs and spill.
+  constexpr bool kPinAcc = D > 128;
 
   // three LDS objects -- the two tile stages and the V rows -- so that the
   // compiler knows which accesses the asynchronous tile loads into one stage
@@ -550,17 +616,48 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     // the row order of the transposing reads below, so P and dS serve as the
     // B operands of the dV and dK products straight from registers
     f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
+    if constexpr (kPinAcc) {
+      // fragments read PD k-steps ahead of their MFMAs, scheduling barriers
+      // between the k-steps: the reads of all k-steps hoisted to the top
+      // would hold 12 registers per k-step
+      constexpr int PD = 2;
+      frag qfr[KSTEPS], dfr[KSTEPS], vfr[KSTEPS];
+      auto rd = [&](auto ic) {
+        constexpr int st = decltype(ic)::value;
+        const int qo = ((st & 1) ? q_odd : q_even) + 64 * (st >> 1);
+        qfr[st] = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + qo));
+        dfr[st] = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + qo));
+        vfr[st] = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(v_lds + v_lane + st * 32));
+      };
+      static_for<0, PD>(rd);
+      static_for<0, KSTEPS>([&](auto ic) {
+        constexpr int st = decltype(ic)::value;
+        if constexpr (st + PD < KSTEPS) rd(std::integral_constant<int, st + PD>{});
+        // (as inline assembly too: with AGPR operands in the kernel the
+        // compiler would give these results AGPRs and copy them out)
+        if constexpr (st == 0) {
+          X::vfirst(s, qfr[st], kf[st]);
+          X::vfirst(dp, dfr[st], vfr[st]);
+        } else {
+          X::vnext(s, qfr[st], kf[st]);
+          X::vnext(dp, dfr[st], vfr[st]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      mfma_drain_v(s, dp);  // before the VALU reads of S and dP
+    } else {
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      const int qo = ((st & 1) ? q_odd : q_even) + 64 * (st >> 1);
-      const frag qfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + qo));
-      const frag dfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + qo));
-      s = M::mma(qfr, kf[st], s);
-      if constexpr (G::V_IN_LDS) {
-        const frag vfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(v_lds + v_lane + st * 32));
-        dp = M::mma(dfr, vfr, dp);
-      } else {
-        dp = M::mma(dfr, vf[st], dp);
+      for (int st = 0; st < KSTEPS; ++st) {
+        const int qo = ((st & 1) ? q_odd : q_even) + 64 * (st >> 1);
+        const frag qfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(qb + qo));
+        const frag dfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(dob + qo));
+        s = M::mma(qfr, kf[st], s);
+        if constexpr (G::V_IN_LDS) {
+          const frag vfr = __builtin_bit_cast(frag, *(FA_LDS u32x4_t*)(v_lds + v_lane + st * 32));
+          dp = M::mma(dfr, vfr, dp);
+        } else {
+          dp = M::mma(dfr, vf[st], dp);
+        }
       }
     }
 
@@ -590,6 +687,34 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     }
 
     // dV^T += dO^T P and dK^T += Q^T dS: two 16-query steps per 32-dim block
+    if constexpr (kPinAcc) {
+      // the same with the transposing reads PD blocks ahead of their MFMAs
+      constexpr int PD = 2, NB = 2 * DBLK;
+      frag dtr[NB], qtr[NB];
+      auto rd = [&](auto ic) {
+        constexpr int j = decltype(ic)::value, u = j / DBLK, db = j % DBLK;
+        FA_LDS char* d0 = dob + (16 * u) * QR + db * 64;
+        FA_LDS char* q0p = qb + (16 * u) * QR + db * 64;
+        const i16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(d0 + t_lo));
+        const i16x4_t dup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(d0 + t_up));
+        const i16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(q0p + t_lo));
+        const i16x4_t qup = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(q0p + t_up));
+        dtr[j] = __builtin_bit_cast(frag, (u32x4_t){__builtin_bit_cast(u32x2_t, dlo)[0], __builtin_bit_cast(u32x2_t, dlo)[1],
+                                                    __builtin_bit_cast(u32x2_t, dup)[0], __builtin_bit_cast(u32x2_t, dup)[1]});
+        qtr[j] = __builtin_bit_cast(frag, (u32x4_t){__builtin_bit_cast(u32x2_t, qlo)[0], __builtin_bit_cast(u32x2_t, qlo)[1],
+                                                    __builtin_bit_cast(u32x2_t, qup)[0], __builtin_bit_cast(u32x2_t, qup)[1]});
+      };
+      static_for<0, PD>(rd);
+      static_for<0, NB>([&](auto ic) {
+        constexpr int j = decltype(ic)::value, u = j / DBLK, db = j % DBLK;
+        if constexpr (j + PD < NB) rd(std::integral_constant<int, j + PD>{});
+        const frag pfr = __builtin_bit_cast(frag, (u32x4_t){pp[4 * u], pp[4 * u + 1], pp[4 * u + 2], pp[4 * u + 3]});
+        const frag sfr = __builtin_bit_cast(frag, (u32x4_t){ps[4 * u], ps[4 * u + 1], ps[4 * u + 2], ps[4 * u + 3]});
+        X::acc_fresh(dvacc[db], dtr[j], pfr);
+        X::acc_fresh(dkacc[db], qtr[j], sfr);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const frag pfr = __builtin_bit_cast(frag, (u32x4_t){pp[4 * u], pp[4 * u + 1], pp[4 * u + 2], pp[4 * u + 3]});
@@ -609,6 +734,7 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
         dvacc[db] = M::mma(__builtin_bit_cast(frag, draw), pfr, dvacc[db]);
         dkacc[db] = M::mma(__builtin_bit_cast(frag, qraw), sfr, dkacc[db]);
       }
+    }
     }
     if (t + 1 < qt_end) stats_store(nb);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
@@ -630,6 +756,10 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   }
 
   // dK = scale * dK^T^T, dV = dV^T^T, rounded to the input type
+  if constexpr (kPinAcc) {  // the last accumulator MFMAs before the VALU reads
+    mfma_drain_a<DBLK>(dvacc);
+    mfma_drain_a<DBLK>(dkacc);
+  }
   if (wave_keys == 0) return;
   const auto rdk = make_rsrc(dkg + (int64_t)kw * a.dk_ss, (wave_keys - 1) * (int32_t)a.dk_ss * 2 + a.head_dim * 2);
   const auto rdv = make_rsrc(dvg + (int64_t)kw * a.dv_ss, (wave_keys - 1) * (int32_t)a.dv_ss * 2 + a.head_dim * 2);
