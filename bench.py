@@ -58,6 +58,7 @@ PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (1 GPU)"
 KERNEL_SOURCES = ["tiled_attention_04_amd/csrc/fa_fwd_kernels.hpp",
                   "tiled_attention_04_amd/csrc/fa_fwd_wide.hpp",
+                  "tiled_attention_04_amd/csrc/fa_mfma_asm.hpp",
                   "tiled_attention_04_amd/csrc/fa_api.hip"]
 PROFILES = os.path.join(ROOT, "profiles")
 # context only: the pages' unfused attention timings on an RTX 3090 (fp32,
