@@ -82,10 +82,10 @@ fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& 
 }
 
 // Instantiated head-dim paddings: the smallest one >= head_dim is used.
-template <typename T, int D, int NW, int OCC>
+template <typename T, int D, int NW, int OCC, bool XB = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_16bit(fa::FwdArgs a) {
-  fa::fa_fwd_16bit_body<T, D, NW>(a);
+  fa::fa_fwd_16bit_body<T, D, NW, XB>(a);
 }
 
 // head_dim 129..256 in one pass: 4 waves of 32 query rows, one per SIMD, Q
@@ -109,7 +109,15 @@ fa_status_t launch_16bit_nw(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
 #define FA_CASE(DP)                                                            \
   if (head_dim <= DP) return launch(fa_fwd_16bit<T, DP, NW, OCC>, grid, 64 * NW, a, stream);
-  FA_CASE(32) FA_CASE(64) FA_CASE(80) FA_CASE(96) FA_CASE(128)
+  FA_CASE(32)
+  // head_dim 33..64 in 4-wave workgroups (small grids): P.V over 96 dims so
+  // that dim 64 carries the row sum (the VALU-bound shape trades 4 MFMAs per
+  // tile for 16 dot products; in 8-wave workgroups it does not pay)
+  if (head_dim <= 64) {
+    if constexpr (NW == 4) return launch(fa_fwd_16bit<T, 64, NW, OCC, true>, grid, 64 * NW, a, stream);
+    else return launch(fa_fwd_16bit<T, 64, NW, OCC>, grid, 64 * NW, a, stream);
+  }
+  FA_CASE(80) FA_CASE(96) FA_CASE(128)
 #undef FA_CASE
   // head_dim > 128: the wide kernel, 4-wave workgroups (128 query rows)
   fa::FwdArgs a4 = a;

@@ -220,13 +220,14 @@ __device__ inline float row_max32(const f32x16_t& a, const f32x16_t& b) {
 // 16-bit inputs (bf16 / f16).  D = head_dim rounded up to 16, NW waves per
 // workgroup, OCC waves per SIMD targeted by the register allocator.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool XB = false>
 struct Tile16 {
   static constexpr int BM = 32 * NW;           // query rows per workgroup
   static constexpr int BN = 64;                // keys per K/V tile
   static constexpr int NT = 64 * NW;           // threads per workgroup
   static constexpr int KSTEPS = D / 16;        // k-steps of the S^T MFMA (16 dims each)
-  static constexpr int DBLK = (D + 31) / 32;   // 32-dim blocks of the O^T accumulator
+  // 32-dim blocks of the O^T accumulator (XB: one more, for the row-sum column)
+  static constexpr int DBLK = (D + 31) / 32 + (XB ? 1 : 0);
   // K rows: stride = 16 (mod 256) bytes, so the 32 lanes reading one 16-byte
   // chunk of 32 consecutive rows fall on distinct bank groups.
   static constexpr int KROW = D * 2 + 16;
@@ -250,20 +251,20 @@ struct Tile16 {
 
 // Body of the 16-bit kernel; the __global__ entry points that instantiate it
 // (with their occupancy attributes) are defined next to the launcher.
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool XB = false>
 __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
-  using G = Tile16<T, D, NW>;
+  using G = Tile16<T, D, NW, XB>;
   using M = Mfma<T>;
   typedef typename M::frag frag;
   constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
   constexpr int KROW = G::KROW, VROW = G::VROW;
   // Row sum by the matrix core where the P.V product pads the head dims (D
-  // not a multiple of 32): V's column D is 1.0 in both LDS stages, so row D
-  // of O^T accumulates the sum of the rounded weights of each query along
-  // with the output, and the VALU row sum (16 dot products per tile and
-  // wave) and its rescale drop out.  The padding columns are written once
-  // and never loaded over.
-  constexpr bool kOnesCol = (D % 32) != 0;
+  // not a multiple of 32, or XB: one 32-dim block added for it): V's column
+  // D is 1.0 in both LDS stages, so row D of O^T accumulates the sum of the
+  // rounded weights of each query along with the output, and the VALU row
+  // sum (16 dot products per tile and wave) and its rescale drop out.  The
+  // padding columns are written once and never loaded over.
+  constexpr bool kOnesCol = (D % 32) != 0 || XB;
 
   __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
   FA_LDS char* lds = (FA_LDS char*)smem;
