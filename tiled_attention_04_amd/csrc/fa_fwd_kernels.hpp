@@ -287,6 +287,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   const int q0 = qt * G::BM;
   const int qw = q0 + wave * 32;        // first query row of this wave
   const int my_q = qw + l32;            // query row of this lane
+  // last key this lane's row may see (the key tail, and causal: its own row)
+  const int key_lim = a.causal ? min(a.seq_k - 1, my_q) : a.seq_k - 1;
   const bool wave_live = qw < a.seq_q;
   const int wave_rows = wave_live ? min(32, a.seq_q - qw) : 0;
 
@@ -405,13 +407,16 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     const int key0 = t * BN;
     const bool need_mask = (key0 + BN > a.seq_k) || (a.causal && key0 + BN - 1 > qw);
     if (need_mask) {
+      // key kb2 32 + 8 (r / 4) + 4 hi + r % 4 of the tile is visible iff its
+      // offset cr = kb2 32 + 8 (r / 4) + r % 4 (a constant, 0..63) is at most
+      // dl: one compare against an inline constant and one select per score
+      const int dl = key_lim - key0 - 4 * hi;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool vis = key < a.seq_k && (!a.causal || key <= my_q);
-          s[kb2][r] = vis ? s[kb2][r] : -INFINITY;
+          const int cr = kb2 * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb2][r] = cr <= dl ? s[kb2][r] : -INFINITY;
         }
     }
     float mx = row_max32(s[0], s[1]);

@@ -125,6 +125,8 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
   const int t0 = min(n_all, split * chunk);
   const int t1 = min(n_all, t0 + chunk);
   const int key_end = min(a.seq_k, t1 * BN);
+  // last key this lane's row may see
+  const int key_lim = a.causal ? min(key_end - 1, qw + l32) : key_end - 1;
 
   // ---- resident Q fragment (B operand of S^T), moved to AGPRs once
   frag qf[KSTEPS];
@@ -230,13 +232,15 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
   auto mask = [&](int t, f32x16_t (&s)[2]) {
     const int key0 = t * BN;
     if ((key0 + BN > key_end) || (a.causal && key0 + BN - 1 > qw)) {
-      const int lim = a.causal ? min(key_end - 1, qw + l32) : key_end - 1;
+      // key key0 + cr + 4 hi (cr = kb2 32 + 8 (r / 4) + r % 4, a constant)
+      // is visible iff cr <= dl
+      const int dl = key_lim - key0 - 4 * hi;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          s[kb2][r] = key <= lim ? s[kb2][r] : -INFINITY;
+          const int cr = kb2 * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb2][r] = cr <= dl ? s[kb2][r] : -INFINITY;
         }
     }
   };
