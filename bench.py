@@ -121,10 +121,10 @@ def cpu_baseline(inp, target_s=15.0):
     mean_row = 4.0 * w.head_dim * ((w.seq_k + 1) / 2 if w.causal else w.seq_k)
     max_rows = w.batch * w.heads * S
     n_rows = 256
-    for _ in range(4):  # grow the sample until it takes a sizeable share of target_s
+    for _ in range(4):  # grow the sample until it takes at least two thirds of target_s
         n_heads = int(min(w.batch * w.heads, max(1, -(-n_rows // S))))
         rows, dt = run(n_heads, min(n_rows, n_heads * S))
-        if dt >= 0.4 * target_s or rows.size >= max_rows:
+        if dt >= (2.0 / 3.0) * target_s or rows.size >= max_rows:
             break
         rate = row_flops(rows) / max(dt, 1e-3)  # oracle FLOP/s on this host
         n_rows = int(min(max_rows, max(2 * n_rows, rate * target_s / mean_row)))
