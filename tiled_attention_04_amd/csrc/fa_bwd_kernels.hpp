@@ -215,6 +215,8 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
   const int qw = q0 + wave * 32;
   const int my_q = qw + l32;
   const int wave_rows = max(0, min(32, a.seq_q - qw));
+  // last key this lane's query sees (the key tail, and causal: its own row)
+  const int key_lim = a.causal ? min(a.seq_k - 1, my_q) : a.seq_k - 1;
   const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + G::BM)) : a.seq_k;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
@@ -355,6 +357,9 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
     const int key0 = t * BN;
     const bool need_mask = (key0 + BN > a.seq_k) || (a.causal && key0 + BN - 1 > qw);
     uint32_t pk[2][8];
+    // key key0 + cr + 4 hi (cr = kb2 32 + 8 (r / 4) + r % 4, a constant) is
+    // visible to this lane's query iff cr <= dl
+    const int dl = key_lim - key0 - 4 * hi;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -362,9 +367,9 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
         float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -L2));
         float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -L2));
         if (need_mask) {
-          const int kk = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          p0 = (kk < a.seq_k && (!a.causal || kk <= my_q)) ? p0 : 0.f;
-          p1 = (kk + 1 < a.seq_k && (!a.causal || kk + 1 <= my_q)) ? p1 : 0.f;
+          const int cr = kb2 * 32 + 8 * (r >> 2) + (r & 3);
+          p0 = cr <= dl ? p0 : 0.f;
+          p1 = cr + 1 <= dl ? p1 : 0.f;
         }
         pk[kb2][r >> 1] = M::pack2(p0 * (dp[kb2][r] - Dl), p1 * (dp[kb2][r + 1] - Dl));
       }
@@ -664,6 +669,10 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     const int qa = t * BQ;
     const int my_k = kw + l32;
     const bool need_mask = (qa + BQ > a.seq_q) || (kw + 32 > a.seq_k) || (a.causal && kw + 31 > qa);
+    // query qa + 4 hi + cq (cq = 8 j + i, a constant) sees this lane's key
+    // iff dlo <= cq <= dhi (a key past seq_k: dhi < 0, seen by nobody)
+    const int dlo = (a.causal ? my_k : 0) - qa - 4 * hi;
+    const int dhi = (my_k < a.seq_k ? a.seq_q - 1 : -1 - 64) - qa - 4 * hi;
     // P = exp2(s c - L2) and dS = P (dP - D) in the input type, paired along queries
     uint32_t pp[8], ps[8];
 #pragma unroll
@@ -677,9 +686,9 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
         float p0 = fast_exp2(__builtin_fmaf(s[r], c, -L4[i]));
         float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -L4[i + 1]));
         if (need_mask) {
-          const int q = qa + row + i;
-          p0 = (q < a.seq_q && my_k < a.seq_k && (!a.causal || my_k <= q)) ? p0 : 0.f;
-          p1 = (q + 1 < a.seq_q && my_k < a.seq_k && (!a.causal || my_k <= q + 1)) ? p1 : 0.f;
+          const int cq = 8 * j + i;
+          p0 = (cq >= dlo && cq <= dhi) ? p0 : 0.f;
+          p1 = (cq + 1 >= dlo && cq + 1 <= dhi) ? p1 : 0.f;
         }
         pp[r >> 1] = M::pack2(p0, p1);
         ps[r >> 1] = M::pack2(p0 * (dp[r] - D4[i]), p1 * (dp[r + 1] - D4[i + 1]));
