@@ -243,7 +243,11 @@ struct Tile16 {
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = BN * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  // the epilogue stages each wave's 32 x D output rows in LDS (row stride
+  // D * 2 + 16 bytes) to store them as whole 16-byte pieces of rows
+  static constexpr int OROW = D * 2 + 16;
+  static constexpr int OBYTES = 32 * OROW;
+  static constexpr int LDS_BYTES = 2 * STAGE > NW * OBYTES ? 2 * STAGE : NW * OBYTES;
   static_assert(D % 16 == 0 && D <= 128, "head_dim padding (wider ones: fa_fwd_wide.hpp)");
   static_assert(KROW % 16 == 0 && VROW % 16 == 0, "16-byte aligned rows");
   static_assert((BN * KSLOTS) % 64 == 0 && (BN * VSLOTS) % 64 == 0, "whole wave loads");
@@ -568,17 +572,33 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   const float inv = 1.0f / l_tot;
   const int32_t onrec = (wave_rows - 1) * (int32_t)a.o_ss * 2 + a.head_dim * 2;
   const auto ro = make_rsrc(og + (int64_t)qw * a.o_ss, onrec);
-  const uint32_t orow = (uint32_t)(l32 * (int32_t)a.o_ss * 2);
+  // O through LDS (every wave is past the last barrier of the key loop, so
+  // the tile stages are free): this lane's 4-dim pieces of query row l32
+  // go to the wave's own 32-row area, then each lane stores whole 16-byte
+  // pieces of rows, consecutive lanes covering consecutive bytes of a row
+  FA_LDS char* const ob = lds + wave * G::OBYTES;
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      if (db * 32 + 8 * g >= D) continue;  // the row-sum block (XB) is not output
       const int d0 = db * 32 + 8 * g + 4 * hi;
-      const uint32_t off = (d0 < a.head_dim && l32 < wave_rows) ? orow + d0 * 2 : kOutOfRange;
       const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
                          M::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+      *(FA_LDS u32x2_t*)(ob + l32 * G::OROW + d0 * 2) = w;
     }
+  constexpr int CPR = D / 8;  // 16-byte pieces per row
+#pragma unroll
+  for (int c0 = 0; c0 < 32 * CPR; c0 += 64) {
+    const int c = c0 + lane;
+    const int row = c / CPR, col = c - (c / CPR) * CPR;
+    if (32 * CPR % 64 == 0 || c < 32 * CPR) {
+      const u32x4_t w = *(FA_LDS u32x4_t*)(ob + row * G::OROW + col * 16);
+      const uint32_t off = (row < wave_rows && col * 8 < a.head_dim)
+                               ? (uint32_t)(row * (int32_t)a.o_ss * 2 + col * 16) : kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
+    }
+  }
   if (hi == 0 && a.lse != nullptr && my_q < a.seq_q)
     a.lse[(int64_t)bh * a.seq_q + my_q] = (m_run + __log2f(l_tot)) * kLn2;
 }
