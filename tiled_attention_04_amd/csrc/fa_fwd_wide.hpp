@@ -454,6 +454,7 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
       if (t + 2 >= t1) break;
     }
     mfma_drain_a<DBLK>(acc);
+    __syncthreads();  // every wave's last reads of the K stages are done
   }
 
   // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
@@ -486,17 +487,31 @@ __device__ __forceinline__ void fa_fwd_wide_body(const FwdArgs& a) {
   const float inv = 1.0f / l_tot;
   const int32_t onrec = (wave_rows - 1) * (int32_t)a.o_ss * 2 + a.head_dim * 2;
   const auto ro = make_rsrc(og + (int64_t)qw * a.o_ss, onrec);
-  const uint32_t orow = (uint32_t)(l32 * (int32_t)a.o_ss * 2);
+  // O through LDS: the barrier after the key loop has freed the K stages,
+  // each of which holds two waves' 32 output rows at the K row stride; then every
+  // lane stores whole 16-byte pieces of rows, consecutive lanes on
+  // consecutive bytes
+  static_assert(G::KBYTES == 2 * 32 * KROW, "two waves' rows per K stage");
+  FA_LDS char* const ob = (wave < 2 ? (FA_LDS char*)k_st0 : (FA_LDS char*)k_st1) + (wave & 1) * 32 * KROW;
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = db * 32 + 8 * g + 4 * hi;
-      const uint32_t off = (d0 < a.head_dim && l32 < wave_rows) ? orow + d0 * 2 : kOutOfRange;
       const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
                          M::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+      *(FA_LDS u32x2_t*)(ob + l32 * KROW + d0 * 2) = w;
     }
+  constexpr int CPR = D / 8;  // 16-byte pieces per row
+#pragma unroll
+  for (int c0 = 0; c0 < 32 * CPR; c0 += 64) {
+    const int c = c0 + lane;
+    const int row = c / CPR, col = c - (c / CPR) * CPR;
+    const u32x4_t w = *(FA_LDS u32x4_t*)(ob + row * KROW + col * 16);
+    const uint32_t off = (row < wave_rows && col * 8 < a.head_dim)
+                             ? (uint32_t)(row * (int32_t)a.o_ss * 2 + col * 16) : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
+  }
   if (hi == 0 && a.lse != nullptr && l32 < wave_rows)
     a.lse[(int64_t)bh * a.seq_q + qw + l32] = (m + __log2f(l_tot)) * kLn2;
 }
