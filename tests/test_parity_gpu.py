@@ -183,11 +183,16 @@ def test_repeat_is_bitwise_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-# ---- large grids at head_dim 97..128: the 64-row-per-wave kernel's domain ----
+# ---- large grids: 8-wave workgroups (at head_dim 64 and 128 with four LDS
+# stages and loads two tiles ahead, a loop unrolled by four key tiles) ----
 
 LARGE_GRID = [
     # (dtype, heads, seq_q, seq_k, head_dim, causal)
     ("bf16", 1024, 200, 333, 128, False),   # one query tile per head, ragged keys
+    ("bf16", 1024, 100, 100, 128, False),   # two key tiles
+    ("bf16", 1024, 256, 500, 128, False),   # eight key tiles: two whole unrolled rounds
+    ("bf16", 1024, 200, 333, 64, True),     # head_dim 64
+    ("fp16", 1024, 250, 777, 48, False),    # head_dim 48 in the 64 slots, 13 key tiles
     ("bf16", 1024, 200, 333, 128, True),
     ("bf16", 512, 300, 129, 128, False),    # a ragged second query tile, 3 key tiles
     ("bf16", 512, 300, 300, 128, True),

@@ -73,6 +73,15 @@ def test_splitk_head_dim_256_shares(dtype, causal, splits):
     splitk_parity(w, splits)
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_splitk_large_grid_shares(head_dim):
+    # 1024 query tiles: 8-wave workgroups, whose shares of 5-6 key tiles
+    # end inside the loop unrolled by four
+    w = synth.custom(f"splitk large grid d{head_dim}", "bf16", "bhsd", 1, 1024, 100, 1000,
+                     head_dim, causal=False, seed=36)
+    splitk_parity(w, 3)
+
+
 def test_splitk_more_splits_than_tiles():
     # causal, 2 key tiles per query tile at most: most shares are empty
     w = synth.custom("splitk empty shares", "bf16", "bhsd", 1, 2, 100, 100, 64, causal=True,

@@ -85,7 +85,9 @@ fa_status_t launch(Kernel kernel, int64_t grid, int threads, const fa::FwdArgs& 
 template <typename T, int D, int NW, int OCC, bool XB = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void fa_fwd_16bit(fa::FwdArgs a) {
-  fa::fa_fwd_16bit_body<T, D, NW, XB>(a);
+  // 8-wave workgroups at head_dim 64 and 128 load two tiles ahead (measured
+  // 3% faster there; slower at 32 and with the row-sum column at 80 and 96)
+  fa::fa_fwd_16bit_body<T, D, NW, XB, NW == 8 && (D == 64 || D == 128)>(a);
 }
 
 // head_dim 129..256 in one pass: 4 waves of 32 query rows, one per SIMD, Q

@@ -23,7 +23,8 @@
 //    which transposes 4 keys x 16 dims per 16-lane group on the fly;
 //  * K/V tiles are double-buffered in LDS, loaded one tile ahead by buffer
 //    loads that write LDS directly, rows padded so the MFMA operand reads of
-//    one wave spread over the banks;
+//    one wave spread over the banks (8-wave workgroups at head_dim 64 and
+//    128: four stages each, loads two tiles ahead);
 //  * keys >= seq_k and (causal) keys > query are masked to -inf; key rows
 //    beyond seq_k and dims beyond head_dim are zero-filled;
 //  * the running max is refreshed lazily: O and l are rescaled only when the
@@ -253,9 +254,24 @@ struct Tile16 {
   static_assert((BN * KSLOTS) % 64 == 0 && (BN * VSLOTS) % 64 == 0, "whole wave loads");
 };
 
+// One LDS object per (Tag, ID): a distinct __shared__ variable, so that the
+// compiler can tell a direct-to-LDS load into one object from reads of
+// another and does not wait for the load before those reads.
+template <typename Tag, int ID, int BYTES>
+__device__ __forceinline__ FA_LDS char* lds_object() {
+  __shared__ __attribute__((aligned(1024))) char buf[BYTES];
+  return (FA_LDS char*)buf;
+}
+
 // Body of the 16-bit kernel; the __global__ entry points that instantiate it
 // (with their occupancy attributes) are defined next to the launcher.
-template <typename T, int D, int NW, bool XB = false>
+//
+// DEEP: the K/V loads run two tiles ahead instead of one.  Four LDS stages
+// each for K and V, the stage of every access a compile-time constant of a
+// four-step unrolled loop; the barrier at the end of step t waits only for
+// the loads issued in step t - 1 (K(t + 2), V(t + 1)), so each load has two
+// steps to land.
+template <typename T, int D, int NW, bool XB = false, bool DEEP = false>
 __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   using G = Tile16<T, D, NW, XB>;
   using M = Mfma<T>;
@@ -270,8 +286,21 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   // padding columns are written once and never loaded over.
   constexpr bool kOnesCol = (D % 32) != 0 || XB;
 
-  __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
-  FA_LDS char* lds = (FA_LDS char*)smem;
+  // LDS areas: without DEEP one object of two stages (K then V each); with
+  // DEEP four K and four V objects.  kbuf / vbuf take a compile-time stage.
+  struct Tag;
+  auto kbuf = [&](auto pc) -> FA_LDS char* {
+    constexpr int P = decltype(pc)::value;
+    if constexpr (DEEP) return lds_object<Tag, P % 4, G::KBYTES>();
+    else return lds_object<Tag, 8, G::LDS_BYTES>() + (P % 2) * G::STAGE;
+  };
+  auto vbuf = [&](auto pc) -> FA_LDS char* {
+    constexpr int P = decltype(pc)::value;
+    if constexpr (DEEP) return lds_object<Tag, 4 + P % 4, G::VBYTES>();
+    else return lds_object<Tag, 8, G::LDS_BYTES>() + (P % 2) * G::STAGE + G::KBYTES;
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -324,58 +353,77 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   // ---- per-lane byte offsets of the direct-to-LDS tile loads (tile independent)
   uint32_t koff[G::KPER], voff[G::VPER];
   bool vlive[G::VPER];  // (ones-column layout) this lane's V chunk lies below dim D
+  // DEEP: every wave issues KPER K and VPER V loads, so that the count per
+  // wave is a compile-time constant; a share beyond the tile's instructions
+  // repeats a valid one (the same bytes to the same place).  (Reading out of
+  // range into a dump area instead measured slower.)
+  auto kinstr = [&](int n) { const int i = wave + NW * n; return DEEP && i >= G::KINSTR ? i % G::KINSTR : i; };
+  auto vinstr = [&](int n) { const int i = wave + NW * n; return DEEP && i >= G::VINSTR ? i % G::VINSTR : i; };
 #pragma unroll
   for (int n = 0; n < G::KPER; ++n) {
-    const int slot = (wave + NW * n) * 64 + lane;
+    const int slot = kinstr(n) * 64 + lane;
     const int row = slot / G::KSLOTS, ch = slot - (slot / G::KSLOTS) * G::KSLOTS;
     koff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.k_ss * 2 + ch * 16) : kOutOfRange;
   }
 #pragma unroll
   for (int n = 0; n < G::VPER; ++n) {
-    const int slot = (wave + NW * n) * 64 + lane;
+    const int slot = vinstr(n) * 64 + lane;
     const int row = slot / G::VSLOTS, ch = slot - (slot / G::VSLOTS) * G::VSLOTS;
     voff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
     vlive[n] = ch * 8 < D;
   }
-  // Tile j's K goes to the K area and its V to the V area of LDS stage j & 1;
-  // rows >= seq_k and dims >= head_dim land as zeros.
-  auto issue_k = [&](int j) {
+  // Tile j's K goes to the K area and its V to the V area of LDS stage
+  // (j - t0) & 1 (DEEP: stage (j - t0) % 4, passed as the compile-time pc);
+  // rows >= seq_k and dims >= head_dim land as zeros.  DEEP issues the same
+  // loads every step: a tile j >= t1 gets an empty range (zeros, no memory
+  // access).
+  auto issue_k = [&](int j, auto pc) {
     const int key0 = j * BN;
     const int rows = min(BN, a.seq_k - key0);
-    const auto rk = make_rsrc(kg + (int64_t)key0 * a.k_ss, (rows - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2);
-    FA_LDS char* kb = lds + ((j - t0) & 1) * G::STAGE;
+    const int32_t nrec = (rows - 1) * (int32_t)a.k_ss * 2 + a.head_dim * 2;
+    const auto rk = make_rsrc(kg + (int64_t)key0 * a.k_ss, (!DEEP || j < t1) ? nrec : 0);
+    FA_LDS char* kb;
+    if constexpr (DEEP) kb = kbuf(pc);
+    else kb = lds_object<Tag, 8, G::LDS_BYTES>() + ((j - t0) & 1) * G::STAGE;
 #pragma unroll
     for (int n = 0; n < G::KPER; ++n)
-      if (wave + NW * n < G::KINSTR)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(kb + (wave + NW * n) * 1024), 16,
+      if (DEEP || wave + NW * n < G::KINSTR)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(kb + kinstr(n) * 1024), 16,
                                                  koff[n], 0, 0, 0);
   };
-  auto issue_v = [&](int j) {
+  auto issue_v = [&](int j, auto pc) {
     const int key0 = j * BN;
     const int rows = min(BN, a.seq_k - key0);
-    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2);
-    FA_LDS char* vb = lds + ((j - t0) & 1) * G::STAGE + G::KBYTES;
+    const int32_t nrec = (rows - 1) * (int32_t)a.v_ss * 2 + a.head_dim * 2;
+    const auto rv = make_rsrc(vg + (int64_t)key0 * a.v_ss, (!DEEP || j < t1) ? nrec : 0);
+    FA_LDS char* vb;
+    if constexpr (DEEP) vb = vbuf(pc);
+    else vb = lds_object<Tag, 8, G::LDS_BYTES>() + ((j - t0) & 1) * G::STAGE + G::KBYTES;
 #pragma unroll
     for (int n = 0; n < G::VPER; ++n)
-      if (wave + NW * n < G::VINSTR && (!kOnesCol || vlive[n]))
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(vb + (wave + NW * n) * 1024), 16,
+      if ((DEEP || wave + NW * n < G::VINSTR) && (!kOnesCol || vlive[n]))
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(vb + vinstr(n) * 1024), 16,
                                                  voff[n], 0, 0, 0);
   };
-  // (ones-column layout) V columns D..32 DBLK - 1 of both stages: 1.0 in
+  // (ones-column layout) V columns D..32 DBLK - 1 of every stage: 1.0 in
   // column D, zeros after it; written once, never loaded over
-  auto pad_cols = [&](int stage) {
+  auto pad_cols = [&](auto pc) {
     if constexpr (kOnesCol) {
       constexpr int C0 = D / 8, NC = 4 * DBLK - D / 8;  // first padding chunk, padding chunks per row
       for (int i = tid; i < BN * NC; i += G::NT) {
         const int row = i / NC, chk = C0 + i % NC;
         const u32x4_t val = {chk == C0 ? M::kOneBits : 0u, 0u, 0u, 0u};
-        *(FA_LDS u32x4_t*)(lds + stage * G::STAGE + G::KBYTES + row * VROW + chk * 16) = val;
+        *(FA_LDS u32x4_t*)(vbuf(pc) + row * VROW + chk * 16) = val;
       }
     }
   };
   if constexpr (kOnesCol) {
-    pad_cols(0);
-    pad_cols(1);
+    pad_cols(Even{});
+    pad_cols(Odd{});
+    if constexpr (DEEP) {
+      pad_cols(std::integral_constant<int, 2>{});
+      pad_cols(std::integral_constant<int, 3>{});
+    }
   }
 
   // ---- online-softmax state (per lane: query l32; both halves agree on m)
@@ -391,9 +439,9 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   const int s16 = lane & 15;
   const int v_lane = (4 * hi + (s16 >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
 
-  // S^T = K Q^T for the two 32-key blocks of the K tile in stage P
-  auto scores = [&](int parity, f32x16_t (&s)[2]) {
-    FA_LDS char* kb = lds + parity * G::STAGE;
+  // S^T = K Q^T for the two 32-key blocks of the K tile in stage pc
+  auto scores = [&](auto pc, f32x16_t (&s)[2]) {
+    FA_LDS char* kb = kbuf(pc);
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = (f32x16_t){};
 #pragma unroll
@@ -459,8 +507,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   };
 
   // O^T += V^T P^T with the V tile in stage P: four 16-key steps per 32-dim block
-  auto pv = [&](int parity, const uint32_t (&pk)[2][8]) {
-    FA_LDS char* vb = lds + parity * G::STAGE + G::KBYTES;
+  auto pv = [&](auto pc, const uint32_t (&pk)[2][8]) {
+    FA_LDS char* vb = vbuf(pc);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const u32x4_t praw = {pk[u >> 1][4 * (u & 1) + 0], pk[u >> 1][4 * (u & 1) + 1],
@@ -483,30 +531,29 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   // VALU work of tile t, so the matrix pipe stays busy while P(t) is formed;
   // then P(t) V(t).  K runs one tile ahead of V in LDS: during step t the
   // loads of K(t+2) and V(t+1) are in flight.
-  using Even = std::integral_constant<int, 0>;
-  using Odd = std::integral_constant<int, 1>;
   auto step = [&](int t, auto parity, auto has_next, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
-    constexpr int P = decltype(parity)::value;
+    using Cur = decltype(parity);
+    using Nxt = std::integral_constant<int, 1 - Cur::value>;
 #ifdef FA_LDS_POISON
     // K(t) (read by S(t) in the previous step) and V(t - 1) (read by P V in
     // the previous step) are free now; K(t + 2) and V(t + 1) refill them
-    lds_poison<G::NT>(lds + P * G::STAGE, G::KBYTES);
-    lds_poison<G::NT>(lds + (1 - P) * G::STAGE + G::KBYTES, G::VBYTES);
+    lds_poison<G::NT>(kbuf(Cur{}), G::KBYTES);
+    lds_poison<G::NT>(vbuf(Nxt{}), G::VBYTES);
     if constexpr (kOnesCol) {  // the padding columns are never reloaded: restore them
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      pad_cols(1 - P);
+      pad_cols(Nxt{});
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #endif
     stats(t, cur);
-    if (t + 2 < t1) issue_k(t + 2);
-    if (t + 1 < t1) issue_v(t + 1);
+    if (t + 2 < t1) issue_k(t + 2, Cur{});
+    if (t + 1 < t1) issue_v(t + 1, Nxt{});
     uint32_t pk[2][8];
-    if constexpr (decltype(has_next)::value) scores(1 - P, nxt);
+    if constexpr (decltype(has_next)::value) scores(Nxt{}, nxt);
     probs(cur, pk);
-    pv(P, pk);
+    pv(Cur{}, pk);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+2) / V(t+1) loads have landed
     __syncthreads();                // ... and everyone's; the areas read in step t are free
   };
@@ -514,24 +561,103 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   using No = std::integral_constant<bool, false>;
 
   f32x16_t sa[2], sb[2];
+
+  // DEEP: every wave issues LMIN = KPER + VPER loads in every step, so
+  // vmcnt <= LMIN at the end of step t leaves only step t's own loads in
+  // flight.
+  constexpr int LMIN = G::KPER + G::VPER;
+  static_assert(LMIN <= 15, "vmcnt immediate");
+  // A barrier that leaves step t's loads in flight: this wave's LDS reads
+  // and stores done (lgkmcnt 0), its loads older than the last LMIN landed,
+  // then s_barrier.  __syncthreads() would add a workgroup release fence,
+  // which waits for every LDS write in flight, the direct-to-LDS loads
+  // included; the empty asm statements keep the compiler from moving LDS
+  // accesses across the barrier instead.
+  auto deep_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0070 | LMIN);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // step I (0..3) of the unrolled loop handles tile t = t0 + 4 m + I (its K
+  // and V in stage I); it loads K(t + 3) over K(t - 1) (read by S(t - 1) two
+  // steps earlier) and V(t + 2) over V(t - 2).  S(t + 1) is always formed
+  // (for the last tile from a stage of zeros, never used) so that every step
+  // has one shape.
+  auto deep_step = [&](int t, auto ic, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    constexpr int I = decltype(ic)::value;
+    using K1 = std::integral_constant<int, (I + 1) % 4>;
+    using K3 = std::integral_constant<int, (I + 3) % 4>;
+    using V0 = std::integral_constant<int, I>;
+    using V2 = std::integral_constant<int, (I + 2) % 4>;
+#ifdef FA_LDS_POISON
+    lds_poison<G::NT>(kbuf(K3{}), G::KBYTES);
+    lds_poison<G::NT>(vbuf(V2{}), G::VBYTES);
+    if constexpr (kOnesCol) {  // the padding columns are never reloaded: restore them
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      pad_cols(V2{});
+    }
+    deep_barrier();  // the poison stores done; step t - 1's loads may fly
+#endif
+    stats(t, cur);
+    issue_k(t + 3, K3{});
+    issue_v(t + 2, V2{});
+    uint32_t pk[2][8];
+    scores(K1{}, nxt);
+    probs(cur, pk);
+    pv(V0{}, pk);
+    deep_barrier();  // this wave's loads of step t - 1 (K(t + 2), V(t + 1)) have landed, and everyone's
+  };
+  auto deep_loop = [&]() {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int t = t0;; t += 4) {
+      deep_step(t, I0{}, sa, sb);
+      if (t + 1 >= t1) break;
+      deep_step(t + 1, I1{}, sb, sa);
+      if (t + 2 >= t1) break;
+      deep_step(t + 2, I2{}, sa, sb);
+      if (t + 3 >= t1) break;
+      deep_step(t + 3, I3{}, sb, sa);
+      if (t + 4 >= t1) break;
+    }
+  };
+
   if (t1 > t0) {
-    issue_k(t0);
-    issue_v(t0);
-    if (t0 + 1 < t1) issue_k(t0 + 1);
+    issue_k(t0, Even{});
+    issue_v(t0, Even{});
+    if constexpr (DEEP) {
+      issue_k(t0 + 1, Odd{});
+      issue_k(t0 + 2, std::integral_constant<int, 2>{});
+      issue_v(t0 + 1, Odd{});
+    } else {
+      if (t0 + 1 < t1) issue_k(t0 + 1, Odd{});
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    scores(0, sa);
-    __syncthreads();  // K(t0) consumed by all waves before the first step loads K(t0+2) over it
-    int t = t0;
-    for (; t + 2 < t1; t += 2) {
-      step(t, Even{}, Yes{}, sa, sb);
-      step(t + 1, Odd{}, Yes{}, sb, sa);
-    }
-    if (t + 1 < t1) {
-      step(t, Even{}, Yes{}, sa, sb);
-      step(t + 1, Odd{}, No{}, sb, sa);
+    scores(Even{}, sa);
+    // K(t0) consumed by all waves before the first step loads K(t0+2) over
+    // it (DEEP: the first step loads into stages not yet used)
+    if constexpr (!DEEP) __syncthreads();
+    if constexpr (DEEP) {
+      deep_loop();
+      __builtin_amdgcn_s_waitcnt(0);  // the last steps' loads (zeros) have landed
+      __syncthreads();                // ... before the epilogue reuses the V stages
     } else {
-      step(t, Even{}, No{}, sa, sb);
+      int t = t0;
+      for (; t + 2 < t1; t += 2) {
+        step(t, Even{}, Yes{}, sa, sb);
+        step(t + 1, Odd{}, Yes{}, sb, sa);
+      }
+      if (t + 1 < t1) {
+        step(t, Even{}, Yes{}, sa, sb);
+        step(t + 1, Odd{}, No{}, sb, sa);
+      } else {
+        step(t, Even{}, No{}, sa, sb);
+      }
     }
   }
 
@@ -576,7 +702,21 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   // the tile stages are free): this lane's 4-dim pieces of query row l32
   // go to the wave's own 32-row area, then each lane stores whole 16-byte
   // pieces of rows, consecutive lanes covering consecutive bytes of a row
-  FA_LDS char* const ob = lds + wave * G::OBYTES;
+  FA_LDS char* ob;
+  int orow = G::OROW;
+  if constexpr (DEEP) {
+    // waves 2 i and 2 i + 1 share V stage i: 64 rows at the K row stride
+    // where it fits, else at the V row stride (>= 2 D bytes)
+    constexpr int OR = G::KROW <= G::VROW ? G::KROW : G::VROW;
+    static_assert(OR >= 2 * D, "two waves' output rows per V stage");
+    orow = OR;
+    const int vi = wave >> 1;
+    ob = (vi == 0 ? vbuf(Even{}) : vi == 1 ? vbuf(Odd{})
+          : vi == 2 ? vbuf(std::integral_constant<int, 2>{}) : vbuf(std::integral_constant<int, 3>{})) +
+         (wave & 1) * 32 * OR;
+  } else {
+    ob = lds_object<Tag, 8, G::LDS_BYTES>() + wave * G::OBYTES;
+  }
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -585,7 +725,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
       const int d0 = db * 32 + 8 * g + 4 * hi;
       const u32x2_t w = {M::pack2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
                          M::pack2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-      *(FA_LDS u32x2_t*)(ob + l32 * G::OROW + d0 * 2) = w;
+      *(FA_LDS u32x2_t*)(ob + l32 * orow + d0 * 2) = w;
     }
   constexpr int CPR = D / 8;  // 16-byte pieces per row
 #pragma unroll
@@ -593,7 +733,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     const int c = c0 + lane;
     const int row = c / CPR, col = c - (c / CPR) * CPR;
     if (32 * CPR % 64 == 0 || c < 32 * CPR) {
-      const u32x4_t w = *(FA_LDS u32x4_t*)(ob + row * G::OROW + col * 16);
+      const u32x4_t w = *(FA_LDS u32x4_t*)(ob + row * orow + col * 16);
       const uint32_t off = (row < wave_rows && col * 8 < a.head_dim)
                                ? (uint32_t)(row * (int32_t)a.o_ss * 2 + col * 16) : kOutOfRange;
       __builtin_amdgcn_raw_buffer_store_b128(w, ro, off, 0, 0);
