@@ -54,7 +54,12 @@ def poisoned_library():
 FWD = [
     ("bf16", "bhsd", 2, 3, 300, 333, 64, True),      # 4-wave workgroups, ragged tails
     ("fp16", "bhsd", 1, 4, 700, 1100, 128, False),   # many key tiles
-    ("bf16", "bhsd", 4, 64, 512, 512, 128, True),    # 8-wave workgroups (large grid)
+    ("bf16", "bhsd", 4, 64, 512, 512, 128, True),    # 4-wave workgroups, 8 key tiles
+    # 8-wave workgroups (>= 1024 of them): four stages, loads two tiles ahead
+    ("bf16", "bhsd", 4, 128, 512, 600, 128, True),   # 4 and 8 key tiles
+    ("fp16", "bhsd", 2, 512, 256, 900, 64, False),   # 15 key tiles, head_dim 64
+    # 8-wave workgroups, two stages (head_dim 80: the row-sum column)
+    ("bf16", "bhsd", 1, 1024, 200, 333, 80, True),
     ("bf16", "bhsd", 1, 2, 150, 190, 80, True),      # head_dim 80 (padded V blocks)
     ("bf16", "bhsd", 1, 2, 150, 190, 256, True),     # head_dim 256 (wide kernel, two V stages)
     ("fp16", "bhsd", 1, 2, 300, 700, 192, False),    # head_dim 192 (wide kernel, three V stages)
