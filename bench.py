@@ -57,6 +57,7 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 409
 PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (1 GPU)"
 KERNEL_SOURCES = ["tiled_attention_04_amd/csrc/fa_fwd_kernels.hpp",
+                  "tiled_attention_04_amd/csrc/fa_fwd_ks2.hpp",
                   "tiled_attention_04_amd/csrc/fa_fwd_wide.hpp",
                   "tiled_attention_04_amd/csrc/fa_mfma_asm.hpp",
                   "tiled_attention_04_amd/csrc/fa_api.hip"]

@@ -219,6 +219,35 @@ def test_large_grid_scales(scale):
     full_parity(synth.make_inputs(w), sm_scale=scale, name=f"large grid sm_scale={scale}")
 
 
+# ---- small grids (at most 256 query tiles of 128 rows): the key tiles of a
+# query tile split between two wave groups of one workgroup, merged at the end ----
+
+KEY_GROUPS = [
+    # (dtype, heads, seq_q, seq_k, head_dim, causal)
+    ("bf16", 2, 100, 65, 128, False),     # two key tiles, the second with one key
+    ("bf16", 2, 300, 200, 64, True),      # causal, fewer keys than queries: 2, 4, 4 tiles
+    ("fp16", 3, 129, 1000, 80, True),     # row-sum column; 2 and 3 tiles (group 1 idles)
+    ("bf16", 4, 257, 777, 96, False),     # 13 tiles, the last ragged
+    ("fp16", 2, 64, 4096, 32, False),     # 64 tiles
+    ("bf16", 3, 200, 130, 48, True),      # head_dim 48 in the 64 slots, 3 tiles
+]
+
+
+@pytest.mark.parametrize("dtype,heads,sq,sk,d,causal", KEY_GROUPS)
+def test_key_groups_in_workgroup(dtype, heads, sq, sk, d, causal):
+    w = synth.custom("key groups", dtype, "bhsd", 1, heads, sq, sk, d, causal=causal,
+                     seed=680 + sq + sk + d)
+    full_parity(synth.make_inputs(w), name=f"key groups {dtype} h={heads} sq={sq} sk={sk} d={d} "
+                                           f"causal={causal}")
+
+
+def test_key_groups_stress_rescales():
+    """Keys scaled x32: the two groups' running maxima drift apart before the merge."""
+    w = synth.custom("key groups stress", "bf16", "bhsd", 1, 4, 256, 2048, 128, causal=False,
+                     seed=690, stress_frac=0.03, stress_factor=32.0)
+    full_parity(synth.make_inputs(w), name="key groups stress x32")
+
+
 # ---- head_dim 193..256: the widest paddings, several key and query tiles ----
 
 HEAD_DIM_256 = [

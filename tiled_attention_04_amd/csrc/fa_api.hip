@@ -11,6 +11,7 @@
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernels.hpp"
+#include "fa_fwd_ks2.hpp"
 #include "fa_fwd_wide.hpp"
 #include "fa_bwd_kernels.hpp"
 #include "fa_fp8_kernels.hpp"
@@ -90,6 +91,14 @@ void fa_fwd_16bit(fa::FwdArgs a) {
   fa::fa_fwd_16bit_body<T, D, NW, XB, NW == 8 && (D == 64 || D == 128)>(a);
 }
 
+// small grids: 8 waves over 128 query rows, the key tiles split between two
+// groups of 4 waves that merge their states at the end
+template <typename T, int D, bool XB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_ks2(fa::FwdArgs a) {
+  fa::fa_fwd_ks2_body<T, D, XB>(a);
+}
+
 // head_dim 129..256 in one pass: 4 waves of 32 query rows, one per SIMD, Q
 // and the O^T accumulator in AGPRs
 template <typename T, int D>
@@ -138,9 +147,29 @@ int waves_16bit(int64_t n_bh, int64_t seq_q, int64_t head_dim) {
   return n_bh * ((seq_q + 255) / 256) >= 1024 ? 8 : 4;
 }
 
+// Grids of at most 256 query tiles of 128 rows (one 8-wave workgroup per
+// CU), without key splitting across workgroups: the in-workgroup key split
+// (two key groups over 128 query rows) halves each workgroup's chain of key
+// tiles.  Larger grids keep 4-wave workgroups, two per CU: there the split
+// costs a second round of workgroups (C3 with 768 tiles: 22% slower).
+template <typename T>
+fa_status_t launch_ks2(fa::FwdArgs& a, int64_t head_dim, void* stream) {
+  a.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
+  const int64_t grid = (int64_t)a.n_bh * a.n_qtiles;
+  a.xcd_remap = (a.n_bh % 8 == 0) ? 1 : 0;
+  if (head_dim <= 32) return launch(fa_fwd_ks2<T, 32, false>, grid, 512, a, stream);
+  if (head_dim <= 64) return launch(fa_fwd_ks2<T, 64, true>, grid, 512, a, stream);
+  if (head_dim <= 80) return launch(fa_fwd_ks2<T, 80, false>, grid, 512, a, stream);
+  if (head_dim <= 96) return launch(fa_fwd_ks2<T, 96, false>, grid, 512, a, stream);
+  return launch(fa_fwd_ks2<T, 128, false>, grid, 512, a, stream);
+}
+
 template <typename T>
 fa_status_t launch_16bit(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   if (waves_16bit(a.n_bh, a.seq_q, head_dim) == 8) return launch_16bit_nw<T, 8>(a, head_dim, stream);
+  if (a.n_splits == 1 && head_dim <= 128 && a.seq_k > 64 &&
+      (int64_t)a.n_bh * ((a.seq_q + 127) / 128) <= 256)
+    return launch_ks2<T>(a, head_dim, stream);
   return launch_16bit_nw<T, 4>(a, head_dim, stream);
 }
 
