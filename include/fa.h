@@ -183,8 +183,10 @@ fa_status_t fa_fwd_splitk_static(const void* q, const void* k, const void* v, vo
 
 /* Number of key splits fa_fwd_splitk uses for num_splits == 0: about one
  * workgroup per CU, at least eight 64-key tiles per split, at most 16; 1
- * when the unsplit grid already has 256 workgroups.  Never fails (1 for empty
- * or invalid sizes). */
+ * when the unsplit grid already has 256 workgroups, and 1 instead of 2 (the
+ * unsplit forward of such small grids already splits each query tile's keys
+ * between two wave groups of its workgroup, without partials or a second
+ * launch).  Never fails (1 for empty or invalid sizes). */
 int fa_fwd_splitk_choose(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
                          int64_t head_dim, int causal);
 

@@ -170,9 +170,12 @@ def test_splitk_sizes_and_choice():
     assert fa.fa_fwd_splitk_workspace(1, 2, 128, 64, 1) == 0
     assert fa.fa_fwd_splitk_workspace(1, 2, 128, 64, 3) == 3 * 2 * 128 * 65 * 4
     assert fa.fa_fwd_splitk_workspace(0, 2, 128, 64, 3) == 0
-    # a large grid needs no splitting; a few query tiles against many keys does
+    # a large grid needs no splitting; a few query tiles against many keys does;
+    # where two splits would do, the unsplit kernel's two key groups per
+    # workgroup do the same without partials (C2)
     assert fa.fa_fwd_splitk_choose(1, 16, 32768, 32768, 128, 1) == 1
-    assert fa.fa_fwd_splitk_choose(1, 16, 1000, 1537, 64, 0) > 1
+    assert fa.fa_fwd_splitk_choose(1, 12, 100, 4096, 64, 0) == 8
+    assert fa.fa_fwd_splitk_choose(1, 16, 1000, 1537, 64, 0) == 1
     assert 1 <= fa.fa_fwd_splitk_choose(1, 1, 10, 100000, 64, 0) <= 16
     assert fa.fa_fwd_splitk_choose(0, 1, 10, 10, 64, 0) == 1
     # an empty problem needs no workspace

@@ -90,7 +90,10 @@ def test_splitk_more_splits_than_tiles():
 
 
 def test_splitk_c2_auto():
-    assert splitk_parity(synth.WORKLOADS["c2"], 0) > 1
+    # C2's choice is 1: the unsplit small-grid kernel splits its keys between
+    # two wave groups of each workgroup instead
+    assert splitk_parity(synth.WORKLOADS["c2"], 0) == 1
+    assert splitk_parity(synth.WORKLOADS["c2"], 2) == 2
 
 
 @pytest.mark.parametrize("seq_q", [10, 100])
