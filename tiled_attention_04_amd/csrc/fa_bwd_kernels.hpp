@@ -584,20 +584,23 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
   const int t_lo = t_row * QR + 16 * (t_ch ^ hi) + t_half;
   const int t_up = (t_row + 8) * QR + 16 * (t_ch ^ hi ^ 2) + t_half;
 
-  // lse * log2e and delta of query tile j: wave 0 loads them (lane = row,
-  // index clamped) while the tile before it is processed, and stores them
-  // next to the tile's Q and dO
+  // lse and delta of query tile j: wave 0 loads them (lane = row, index
+  // clamped) while the tile before it is processed, and stores lse * log2e
+  // and delta next to the tile's Q and dO.  The loads go out before the
+  // tile's Q / dO loads and nothing uses them until the store at the end of
+  // the step: loads complete in order, so a use right after them would wait
+  // for the whole next tile as well.
   float ld_l = 0.f, ld_d = 0.f;
   auto stats_load = [&](int j) {
     if (wave == 0) {
       const int qi = min(j * BQ + l32, a.seq_q - 1);
-      ld_l = lseg[qi] * kLog2e;
+      ld_l = lseg[qi];
       ld_d = delg[qi];
     }
   };
   auto stats_store = [&](FA_LDS char* qb) {
     if (wave == 0 && hi == 0) {
-      *(FA_LDS float*)(qb + G::LD_OFF + l32 * 4) = ld_l;
+      *(FA_LDS float*)(qb + G::LD_OFF + l32 * 4) = ld_l * kLog2e;
       *(FA_LDS float*)(qb + G::LD_OFF + BQ * 4 + l32 * 4) = ld_d;
     }
   };
@@ -611,8 +614,8 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     __syncthreads();
 #endif
     if (t + 1 < qt_end) {
-      issue(t + 1, nb);
       stats_load(t + 1);
+      issue(t + 1, nb);
     }
     FA_LDS char* dob = qb + G::TBYTES;
 
