@@ -151,7 +151,8 @@ int waves_16bit(int64_t n_bh, int64_t seq_q, int64_t head_dim) {
 // CU), without key splitting across workgroups: the in-workgroup key split
 // (two key groups over 128 query rows) halves each workgroup's chain of key
 // tiles.  Larger grids keep 4-wave workgroups, two per CU: there the split
-// costs a second round of workgroups (C3 with 768 tiles: 22% slower).
+// costs a second round of workgroups (bf16 [4, 12, 2048] causal, head_dim
+// 64, 768 tiles: 22% slower).
 template <typename T>
 fa_status_t launch_ks2(fa::FwdArgs& a, int64_t head_dim, void* stream) {
   a.n_qtiles = (int32_t)((a.seq_q + 127) / 128);
@@ -186,7 +187,8 @@ int choose_splits(int64_t n_bh, int64_t seq_q, int64_t seq_k, int64_t head_dim, 
   s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 8));
   // two splits are what the unsplit small-grid kernel does inside each
   // workgroup (two key groups, merged in LDS), without the partials and the
-  // second launch: C2 21 us unsplit against 25.6 us with two splits
+  // second launch: fp16, 16 heads, 1000 queries x 1537 keys, head_dim 64,
+  // runs in 21 us unsplit against 25.6 us with two splits
   if (s == 2 && head_dim <= 128) s = 1;
   return (int)std::min<int64_t>(s, 16);
 }

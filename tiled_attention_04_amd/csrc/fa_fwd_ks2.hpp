@@ -11,7 +11,9 @@
 //
 // MI355X design (not from the pages): a grid of a few hundred 4-wave
 // workgroups leaves each wave alone on its SIMD for a long chain of key
-// tiles (C2: 128 workgroups, 25 tiles; C3: the causal tail of 32 tiles).
+// tiles (fp16, 16 heads, 1000 queries x 1537 keys, head_dim 64: 128
+// workgroups of 25 key tiles each; bf16 [4, 12, 2048] causal: a tail of 32
+// tiles).
 // Here a workgroup of 8 waves serves the same 128 query rows: waves 0-3
 // (group 0) walk the even key tiles of the query tile, waves 4-7 (group 1)
 // the odd ones, two waves per SIMD, half the chain each, with no workspace
