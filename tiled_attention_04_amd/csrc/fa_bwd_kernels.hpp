@@ -360,18 +360,36 @@ __device__ __forceinline__ void fa_bwd_dq_body(const BwdArgs& a) {
     // key key0 + cr + 4 hi (cr = kb2 32 + 8 (r / 4) + r % 4, a constant) is
     // visible to this lane's query iff cr <= dl
     const int dl = key_lim - key0 - 4 * hi;
+    // the masks in one branch after all the exponentials, so that the
+    // exponentials form one block of straight-line code with the MFMAs
+    // (head_dim 128: dS too before the branch, which measured faster there;
+    // the other widths keep the products after it)
+    constexpr bool kEarlyDs = D == 128;
+    float pe[2][16];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pe[kb2][r] = fast_exp2(__builtin_fmaf(s[kb2][r], c, -L2));
+        if constexpr (kEarlyDs) pe[kb2][r] *= dp[kb2][r] - Dl;
+      }
+    if (need_mask) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cr = kb2 * 32 + 8 * (r >> 2) + (r & 3);
+          pe[kb2][r] = cr <= dl ? pe[kb2][r] : 0.f;
+        }
+    }
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float p0 = fast_exp2(__builtin_fmaf(s[kb2][r], c, -L2));
-        float p1 = fast_exp2(__builtin_fmaf(s[kb2][r + 1], c, -L2));
-        if (need_mask) {
-          const int cr = kb2 * 32 + 8 * (r >> 2) + (r & 3);
-          p0 = cr <= dl ? p0 : 0.f;
-          p1 = cr + 1 <= dl ? p1 : 0.f;
-        }
-        pk[kb2][r >> 1] = M::pack2(p0 * (dp[kb2][r] - Dl), p1 * (dp[kb2][r + 1] - Dl));
+        if constexpr (kEarlyDs)
+          pk[kb2][r >> 1] = M::pack2(pe[kb2][r], pe[kb2][r + 1]);
+        else
+          pk[kb2][r >> 1] = M::pack2(pe[kb2][r] * (dp[kb2][r] - Dl), pe[kb2][r + 1] * (dp[kb2][r + 1] - Dl));
       }
 
     // dQ^T += K^T dS^T: four 16-key steps per 32-dim block
@@ -677,24 +695,44 @@ __device__ __forceinline__ void fa_bwd_dkv_body(const BwdArgs& a) {
     const int dlo = (a.causal ? my_k : 0) - qa - 4 * hi;
     const int dhi = (my_k < a.seq_k ? a.seq_q - 1 : -1 - 64) - qa - 4 * hi;
     // P = exp2(s c - L2) and dS = P (dP - D) in the input type, paired along queries
+    // (the masks in one branch after all the exponentials, so that the
+    // exponentials form one block of straight-line code with the MFMAs)
+    // (head_dim 128: dS too before the branch, which measured faster there;
+    // the other widths keep the products after it)
+    constexpr bool kEarlyDs = D == 128;
     uint32_t pp[8], ps[8];
+    float pe[16], ds[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = 8 * j + 4 * hi;
-      const f32x4_t L4 = *(FA_LDS f32x4_t*)(qb + G::LD_OFF + row * 4);
-      const f32x4_t D4 = *(FA_LDS f32x4_t*)(qb + G::LD_OFF + BQ * 4 + row * 4);
+      const f32x4_t L4 = *(FA_LDS f32x4_t*)(qb + G::LD_OFF + (8 * j + 4 * hi) * 4);
+      const f32x4_t D4 = *(FA_LDS f32x4_t*)(qb + G::LD_OFF + BQ * 4 + (8 * j + 4 * hi) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pe[4 * j + i] = fast_exp2(__builtin_fmaf(s[4 * j + i], c, -L4[i]));
+        if constexpr (kEarlyDs) ds[4 * j + i] = pe[4 * j + i] * (dp[4 * j + i] - D4[i]);
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int cq = 8 * (r >> 2) + (r & 3);
+        const bool vis = cq >= dlo && cq <= dhi;
+        pe[r] = vis ? pe[r] : 0.f;
+        if constexpr (kEarlyDs) ds[r] = vis ? ds[r] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t D4 = *(FA_LDS f32x4_t*)(qb + G::LD_OFF + BQ * 4 + (8 * j + 4 * hi) * 4);
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         const int r = 4 * j + i;
-        float p0 = fast_exp2(__builtin_fmaf(s[r], c, -L4[i]));
-        float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -L4[i + 1]));
-        if (need_mask) {
-          const int cq = 8 * j + i;
-          p0 = (cq >= dlo && cq <= dhi) ? p0 : 0.f;
-          p1 = (cq + 1 >= dlo && cq + 1 <= dhi) ? p1 : 0.f;
+        if constexpr (!kEarlyDs) {
+          ds[r] = pe[r] * (dp[r] - D4[i]);
+          ds[r + 1] = pe[r + 1] * (dp[r + 1] - D4[i + 1]);
         }
-        pp[r >> 1] = M::pack2(p0, p1);
-        ps[r >> 1] = M::pack2(p0 * (dp[r] - D4[i]), p1 * (dp[r + 1] - D4[i + 1]));
+        pp[r >> 1] = M::pack2(pe[r], pe[r + 1]);
+        ps[r >> 1] = M::pack2(ds[r], ds[r + 1]);
       }
     }
 
