@@ -8,9 +8,12 @@ HBM before the timed region starts.
 
 Prints one JSON line:
   value      attention TFLOP/s = 4*b*h*s_q*s_k*d (halved for causal) / time
-  roofline   the kernel's achieved TFLOP/s against the MI355X dense bf16 MFMA
-             peak, with HBM traffic from rocprofv3 counters when they were
-             taken on the current kernel source
+  roofline   the kernel's achieved TFLOP/s against the MI355X dense MFMA
+             peak of the input type, with HBM traffic from rocprofv3 counters
+             when they were taken on the current kernel source; a workload
+             whose algorithmic bytes (Q, K, V read once, O and lse written
+             once) take longer at 8 TB/s than its FLOPs at that peak (the
+             short-query shapes) reports GB/s against the HBM bound instead
   cpu_baseline  the CPU oracle (C, double, OpenMP) timed on a bounded sample
              of the same workload on this host
 
@@ -24,7 +27,8 @@ Other modes:
                         against the oracle over EVERY row; C5's oracle runs in
                         chunks of heads, about a minute on 16 host cores)
   --workload c1|c2|c3|c4   time another workload (not the default line); also
-                        short100 / short10 (few queries against 4096 keys) and
+                        short100 / short10 (few queries against 4096 keys),
+                        short10_h800 (the same with 800 heads) and
                         c5_e5m2 (the default workload in float8 e5m2, V passed
                         key-major; roofline against the dense fp8 MFMA peak)
                         and hd256 (bf16 [1,16,8192,256] causal: the kernel of
@@ -55,6 +59,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: 256 CU x 2.4 GHz x 8192 FLOP/clk
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 matrix (MFMA) peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E bandwidth
 METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (1 GPU)"
 KERNEL_SOURCES = ["tiled_attention_04_amd/csrc/fa_fwd_kernels.hpp",
                   "tiled_attention_04_amd/csrc/fa_fwd_ks2.hpp",
@@ -345,11 +351,35 @@ def time_launches(step, stream, steps, warmup):
     return region0.elapsed_time(region1) / steps, per_launch, t_wall
 
 
+def algorithmic_bytes(w):
+    """HBM bytes a launch must move at least: Q, K, V read once and O written
+    once in the storage type, the fp32 lse written once."""
+    eb = {"fp32": 4, "fp16": 2, "bf16": 2, "e5m2": 1}[w.dtype]
+    return w.batch * w.heads * ((2 * w.seq_q + 2 * w.seq_k) * w.head_dim * eb + 4 * w.seq_q)
+
+
+def roofline(w, key, splits, per_launch, peak):
+    """The bound of the launch (HBM bytes or MFMA FLOPs, whichever takes
+    longer at the MI355X peaks) and the achieved fraction of it."""
+    flops, nbytes = w.flops(), algorithmic_bytes(w)
+    ms_avg = sum(per_launch) / len(per_launch)
+    timing = {"kernel_ms_avg": round(ms_avg, 5),
+              "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
+              "kernel_ms_min": round(per_launch[0], 5)}
+    traffic = load_traffic(key) if splits == 1 else None
+    if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12):
+        achieved = nbytes / (ms_avg * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": nbytes, **timing}
+    achieved = flops / (ms_avg * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic, **timing}
+
+
 def bench_line(w, key, steps, warmup, splits, ms_per_step, per_launch, peak):
     flops = w.flops()
-    ms_avg = sum(per_launch) / len(per_launch)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (ms_avg * 1e-3) / 1e12
     return {
         "metric": METRIC,
         "value": round(value, 3),
@@ -367,12 +397,7 @@ def bench_line(w, key, steps, warmup, splits, ms_per_step, per_launch, peak):
                    "seq_q": w.seq_q, "seq_k": w.seq_k, "head_dim": w.head_dim,
                    "causal": w.causal, "sm_scale": w.sm_scale, "flops_per_step": flops},
         "pct_of_peak": round(100.0 * value / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": load_traffic(key) if splits == 1 else None,
-                     "kernel_ms_avg": round(ms_avg, 5),
-                     "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
-                     "kernel_ms_min": round(per_launch[0], 5)},
+        "roofline": roofline(w, key, splits, per_launch, peak),
         "context": {"rtx3090_unfused_per_call": CONTEXT_RTX3090},
     }
 
@@ -395,7 +420,7 @@ class Setup:
         else:
             v = upload(w, self.inp.v, dev)
         self.q, self.k, self.v = q, k, v
-        self.peak = PEAK_FP8_TFLOPS if w.dtype == "e5m2" else PEAK_BF16_TFLOPS
+        self.peak = {"e5m2": PEAK_FP8_TFLOPS, "fp32": PEAK_FP32_TFLOPS}.get(w.dtype, PEAK_BF16_TFLOPS)
         self.layout = layout = "shd" if w.layout == "shd" else "bhsd"
         self.o = o = torch.empty_like(q)
         self.lse = lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
@@ -443,8 +468,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c5",
-                    choices=["c1", "c2", "c3", "c4", "c5", "short100", "short10", "c5_e5m2",
-                             "hd256"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "short100", "short10", "short10_h800",
+                             "c5_e5m2", "hd256"])
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")

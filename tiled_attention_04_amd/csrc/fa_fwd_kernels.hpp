@@ -547,13 +547,26 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #endif
-    stats(t, cur);
+    // 4-wave workgroups (the small grids of short sequences): a wave without
+    // query rows only loads its share of the tiles; its matrix and softmax
+    // work would take LDS reads and SIMD time from the waves that have rows.
+    // (The 8-wave kernel, whose grids are large, and head_dim 128, whose
+    // registers are nearly all taken, keep one path: the branch measured
+    // 2-3% slower there.)
+    const bool work = NW != 4 || D == 128 || wave_live;
+    if (work) stats(t, cur);
     if (t + 2 < t1) issue_k(t + 2, Cur{});
     if (t + 1 < t1) issue_v(t + 1, Nxt{});
-    uint32_t pk[2][8];
-    if constexpr (decltype(has_next)::value) scores(Nxt{}, nxt);
-    probs(cur, pk);
-    pv(Cur{}, pk);
+    if (work) {
+      uint32_t pk[2][8];
+      if constexpr (decltype(has_next)::value) scores(Nxt{}, nxt);
+      probs(cur, pk);
+      pv(Cur{}, pk);
+    } else {
+      // (defined on both paths, so that the registers of the tile before
+      // are not kept alive for the merge)
+      nxt[0] = nxt[1] = (f32x16_t){};
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+2) / V(t+1) loads have landed
     __syncthreads();                // ... and everyone's; the areas read in step t are free
   };

@@ -288,13 +288,18 @@ __device__ __forceinline__ void fa_fwd_ks2_body(const FwdArgs& a) {
     __syncthreads();
 #endif
     if (j < Jg) {
-      stats(tile(j), cur);
+      // a wave without query rows only loads its share of the tiles
+      if (wave_live) stats(tile(j), cur);
       if (j + 2 < Jg) issue_k(j + 2, Cur{});
       if (j + 1 < Jg) issue_v(j + 1, Nxt{});
-      uint32_t pk[2][8];
-      scores(Nxt{}, nxt);
-      probs(cur, pk);
-      pv(Cur{}, pk);
+      if (wave_live) {
+        uint32_t pk[2][8];
+        scores(Nxt{}, nxt);
+        probs(cur, pk);
+        pv(Cur{}, pk);
+      } else {
+        nxt[0] = nxt[1] = (f32x16_t){};  // (defined on both paths)
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
     __syncthreads();                // ... and everyone's; the areas read in step j are free

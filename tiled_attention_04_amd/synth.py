@@ -89,6 +89,9 @@ EXTRA_WORKLOADS = {
                          "shd", 1, 12, 100, 4096, 64, 1.0, 0.5, False, seed=41),
     "short10": Workload("fp16 s_q=10 s_k=4096 h=12 d=64 seq-heads-d, non-causal", "fp16",
                         "shd", 1, 12, 10, 4096, 64, 1.0, 0.5, False, seed=42),
+    # the issue's largest head count: each head's 4096 keys read for 10 queries
+    "short10_h800": Workload("fp16 s_q=10 s_k=4096 h=800 d=64 seq-heads-d, non-causal", "fp16",
+                             "shd", 1, 800, 10, 4096, 64, 1.0, 0.5, False, seed=43),
     # the long causal workload with every input stored in float8 e5m2 (the
     # fp8 variant of the tutorial's kernel): same draws, rounded to e5m2
     "c5_e5m2": Workload("e5m2 [1,16,32768,128] causal, 1% of K rows x8", "e5m2", "bhsd", 1, 16,
