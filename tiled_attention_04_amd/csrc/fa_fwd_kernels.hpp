@@ -579,7 +579,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   // vmcnt <= LMIN at the end of step t leaves only step t's own loads in
   // flight.
   constexpr int LMIN = G::KPER + G::VPER;
-  static_assert(LMIN <= 15, "vmcnt immediate");
+  static_assert(!DEEP || LMIN <= 15, "vmcnt immediate");
   // A barrier that leaves step t's loads in flight: this wave's LDS reads
   // and stores done (lgkmcnt 0), its loads older than the last LMIN landed,
   // then s_barrier.  __syncthreads() would add a workgroup release fence,
