@@ -219,6 +219,26 @@ def test_large_grid_scales(scale):
     full_parity(synth.make_inputs(w), sm_scale=scale, name=f"large grid sm_scale={scale}")
 
 
+# ---- 4-wave workgroups whose last query tile leaves waves without rows (they
+# load their share of the tiles and skip the compute) ----
+
+ROWLESS_WAVES = [
+    # (dtype, heads, seq_q, seq_k, head_dim, causal)
+    ("bf16", 300, 200, 333, 80, True),     # tile 1: wave 2 has 8 rows, wave 3 none
+    ("fp16", 400, 40, 500, 64, False),     # waves 2 and 3 without rows in every workgroup
+    ("bf16", 280, 100, 64, 96, True),      # one key tile, wave 3 without rows
+    ("fp16", 300, 33, 700, 32, True),      # causal, 33 queries: one row in wave 1
+]
+
+
+@pytest.mark.parametrize("dtype,heads,sq,sk,d,causal", ROWLESS_WAVES)
+def test_rowless_waves(dtype, heads, sq, sk, d, causal):
+    w = synth.custom("rowless waves", dtype, "bhsd", 1, heads, sq, sk, d, causal=causal,
+                     std=0.5 if dtype == "fp16" else 1.0, seed=690 + sq + sk + d)
+    full_parity(synth.make_inputs(w), name=f"rowless waves {dtype} h={heads} sq={sq} sk={sk} "
+                                           f"d={d} causal={causal}")
+
+
 # ---- small grids (at most 256 query tiles of 128 rows): the key tiles of a
 # query tile split between two wave groups of one workgroup, merged at the end ----
 
