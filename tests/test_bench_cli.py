@@ -1,6 +1,7 @@
-"""bench.py's command line on the CPU: more than one GPU is refused with a
-message and a non-zero status, and the counter summariser reduces a
-rocprofv3 counter CSV to per-kernel means."""
+"""bench.py on the CPU: more than one GPU is refused with a message and a
+non-zero status, the counter summariser reduces a rocprofv3 counter CSV to
+per-kernel means, and the roofline takes the bound (HBM bytes or MFMA FLOPs)
+that a launch's work needs longest for."""
 import json
 import os
 import subprocess
