@@ -134,6 +134,18 @@ def test_bwd_c4_shape():
     full_bwd_parity(w)
 
 
+@pytest.mark.parametrize("dtype,sq,sk,d,causal", [
+    ("fp16", 10, 600, 64, False),    # one query tile, 10 rows: most of the dQ workgroup has no rows
+    ("bf16", 33, 300, 80, True),     # causal, keys past the last query seen by nobody
+    ("bf16", 1, 257, 128, False),    # a single query against two key blocks
+])
+def test_bwd_short_queries_many_heads(dtype, sq, sk, d, causal):
+    # few queries over many heads (the short-query shapes of the issue)
+    w = synth.custom("bwd short queries", dtype, "bhsd", 1, 96, sq, sk, d, causal=causal,
+                     std=0.5 if dtype == "fp16" else 1.0, seed=14 + sq + d)
+    full_bwd_parity(w)
+
+
 def test_bwd_shd_layout_distinct_head_strides():
     # [seq, heads, d] with seq_q != seq_k: the head strides of q and k differ
     w = synth.custom("bwd fp16 shd", "fp16", "shd", 1, 4, 300, 417, 64, sm_scale=0.5, seed=9)
