@@ -92,6 +92,8 @@ __device__ __forceinline__ void fa_fwd_e5m2_body(const FwdArgs& a) {
   const int q0 = qt * G::BM;
   const int qw = q0 + wave * 32;
   const int my_q = qw + l32;
+  // last key this lane's row may see (the key tail, and causal: its own row)
+  const int key_lim = a.causal ? min(a.seq_k - 1, my_q) : a.seq_k - 1;
   const bool wave_live = qw < a.seq_q;
   const int wave_rows = wave_live ? min(32, a.seq_q - qw) : 0;
   const int kv_end = a.causal ? min(a.seq_k, min(a.seq_q, q0 + G::BM)) : a.seq_k;
@@ -195,14 +197,13 @@ __device__ __forceinline__ void fa_fwd_e5m2_body(const FwdArgs& a) {
   auto stats = [&](int t, f32x16_t (&s)[2]) {
     const int key0 = t * BN;
     if ((key0 + BN > a.seq_k) || (a.causal && key0 + BN - 1 > qw)) {
+      // key 32 kb2 + 16 hi + r is visible iff its offset 32 kb2 + r (a
+      // constant) is at most dl: one compare and one select per score
+      const int dl = key_lim - key0 - 16 * hi;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb2 * 32 + 16 * hi + r;
-          const bool vis = key < a.seq_k && (!a.causal || key <= my_q);
-          s[kb2][r] = vis ? s[kb2][r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) s[kb2][r] = kb2 * 32 + r <= dl ? s[kb2][r] : -INFINITY;
     }
     const float m_tile = xlane_max(row_max32(s[0], s[1])) * c;
     const float m_new = __builtin_elementwise_maximum(m_run, m_tile);
