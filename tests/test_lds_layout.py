@@ -128,3 +128,58 @@ def test_forward_tile_strides(d):
             s16 = lane & 15
             addrs.append((s16 >> 2) * vr + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2 + 64 * db)
         assert conflict_free(addrs, 8)
+
+
+def lds_swizzle(r):
+    """Slot permutation of the 16 chunks of a 256-byte row (the head_dim-128
+    forward with K/V loads two tiles ahead): chunk c of row r sits at slot
+    c ^ lds_swizzle(r)."""
+    return ((r & 3) << 2) | ((r >> 2) & 3)
+
+
+def test_forward_swizzled_256_byte_rows():
+    """head_dim 128, 64-row K and V tiles at 256 bytes per row without padding:
+    (1) the 16 direct-to-LDS loads of 1 KiB place every chunk exactly once;
+    (2) the K row reads and the V transposing reads, addressed as the kernel
+    does, find the chunks of the unswizzled layout; (3) neither conflicts."""
+    R, rows, ksteps, dblk = 256, 64, 8, 4
+    # (1) load slot -> (row, chunk): slot p of row r holds chunk p ^ lds_swizzle(r)
+    placed = set()
+    for inst in range(16):
+        for lane in range(64):
+            slot = inst * 64 + lane
+            r, p = divmod(slot, 16)
+            placed.add((r, p ^ lds_swizzle(r)))
+    assert placed == {(r, c) for r in range(rows) for c in range(16)}
+
+    def chunk_at(addr):
+        r, off = divmod(addr, R)
+        p, b = divmod(off, 16)
+        return r, p ^ lds_swizzle(r), b
+
+    # (2) + (3) K row reads: lane (l32, hi), k-step st, 32-row block kb2
+    for kb2 in range(2):
+        for st in range(ksteps):
+            addrs = []
+            for lane in range(64):
+                l32, hi = lane & 31, lane >> 5
+                a = l32 * R + 16 * ((2 * st + hi) ^ lds_swizzle(l32)) + kb2 * 32 * R
+                assert chunk_at(a) == (kb2 * 32 + l32, 2 * st + hi, 0)
+                addrs.append(a)
+            for g in range(4):
+                assert conflict_free(addrs[16 * g:16 * g + 16], 16)
+    # V transposing reads: 16-row group u, 32-dim block db, rows r and r + 8
+    for u in range(rows // 16):
+        for db in range(dblk):
+            for upper in (False, True):
+                addrs = []
+                for lane in range(64):
+                    hi, s16 = lane >> 5, lane & 15
+                    r = 4 * hi + (s16 >> 2) + (8 if upper else 0)
+                    byte = 32 * ((lane >> 4) & 1) + 8 * (s16 & 3)
+                    c = (byte >> 4) + 4 * db
+                    a = r * R + 16 * (c ^ lds_swizzle(r)) + (byte & 15) + 16 * u * R
+                    assert chunk_at(a) == (16 * u + r, c, byte & 15)
+                    addrs.append(a)
+                for g in range(2):
+                    assert conflict_free(addrs[32 * g:32 * g + 32], 8)

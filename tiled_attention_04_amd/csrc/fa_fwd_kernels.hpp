@@ -173,6 +173,13 @@ constexpr int tr_row_stride(int min_bytes) {
   return st;
 }
 
+// Slot permutation of the 16 chunks of a 256-byte row r: the high two bits
+// of the chunk index are XORed with r % 4, the low two with (r / 4) % 4.
+// 16 consecutive rows read at one chunk land on 16 distinct slots (row
+// reads of 16 lanes per cycle), and the four rows of a transposing read's
+// 32 lanes land in four distinct 64-byte windows.
+__device__ __host__ constexpr int lds_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // ---------------------------------------------------------------------------
 // Buffer-resource helpers.  A raw buffer load whose byte offset lies at or
 // beyond num_records returns zeros without touching memory, which gives
@@ -221,7 +228,7 @@ __device__ inline float row_max32(const f32x16_t& a, const f32x16_t& b) {
 // 16-bit inputs (bf16 / f16).  D = head_dim rounded up to 16, NW waves per
 // workgroup, OCC waves per SIMD targeted by the register allocator.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NW, bool XB = false>
+template <typename T, int D, int NW, bool XB = false, bool SWZ = false>
 struct Tile16 {
   static constexpr int BM = 32 * NW;           // query rows per workgroup
   static constexpr int BN = 64;                // keys per K/V tile
@@ -231,10 +238,14 @@ struct Tile16 {
   static constexpr int DBLK = (D + 31) / 32 + (XB ? 1 : 0);
   // K rows: stride = 16 (mod 256) bytes, so the 32 lanes reading one 16-byte
   // chunk of 32 consecutive rows fall on distinct bank groups.
-  static constexpr int KROW = D * 2 + 16;
   // V rows: stride = 64 or 192 (mod 256) bytes, so the rows gathered by a
   // transposing read fall on distinct banks.
-  static constexpr int VROW = tr_row_stride(DBLK * 64);
+  // SWZ (head_dim 128): unpadded 256-byte rows, 16-byte chunk c of row r at
+  // slot c ^ lds_swizzle(r) instead: 16 loads of 1 KiB per tile, which
+  // eight waves issue two each.
+  static constexpr int KROW = SWZ ? D * 2 : D * 2 + 16;
+  static constexpr int VROW = SWZ ? DBLK * 64 : tr_row_stride(DBLK * 64);
+  static_assert(!SWZ || (KROW == 256 && VROW == 256), "the swizzle is for 256-byte rows");
   static constexpr int KSLOTS = KROW / 16;     // 16-byte LDS slots per K row (incl. padding)
   static constexpr int VSLOTS = VROW / 16;
   static constexpr int KINSTR = BN * KSLOTS / 64;  // wave-wide 1 KiB loads per K tile
@@ -273,7 +284,8 @@ __device__ __forceinline__ FA_LDS char* lds_object() {
 // steps to land.
 template <typename T, int D, int NW, bool XB = false, bool DEEP = false>
 __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
-  using G = Tile16<T, D, NW, XB>;
+  constexpr bool SWZ = DEEP && D == 128;  // unpadded swizzled rows (no surplus loads)
+  using G = Tile16<T, D, NW, XB, SWZ>;
   using M = Mfma<T>;
   typedef typename M::frag frag;
   constexpr int BN = G::BN, KSTEPS = G::KSTEPS, DBLK = G::DBLK;
@@ -362,13 +374,15 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 #pragma unroll
   for (int n = 0; n < G::KPER; ++n) {
     const int slot = kinstr(n) * 64 + lane;
-    const int row = slot / G::KSLOTS, ch = slot - (slot / G::KSLOTS) * G::KSLOTS;
+    const int row = slot / G::KSLOTS;
+    const int ch = (slot - row * G::KSLOTS) ^ (SWZ ? lds_swizzle(row) : 0);  // the chunk this slot holds
     koff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.k_ss * 2 + ch * 16) : kOutOfRange;
   }
 #pragma unroll
   for (int n = 0; n < G::VPER; ++n) {
     const int slot = vinstr(n) * 64 + lane;
-    const int row = slot / G::VSLOTS, ch = slot - (slot / G::VSLOTS) * G::VSLOTS;
+    const int row = slot / G::VSLOTS;
+    const int ch = (slot - row * G::VSLOTS) ^ (SWZ ? lds_swizzle(row) : 0);
     voff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
     vlive[n] = ch * 8 < D;
   }
@@ -436,8 +450,27 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 
   // lane-constant LDS offsets of the MFMA operand reads
   const int k_lane = l32 * KROW + hi * 16;
+  // SWZ: the byte offset of chunk 2 st + hi of row l32 (and of row 32 + l32)
+  int k_swz[SWZ ? KSTEPS : 1];
+  if constexpr (SWZ) {
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) k_swz[st] = l32 * KROW + 16 * ((2 * st + hi) ^ lds_swizzle(l32));
+  }
   const int s16 = lane & 15;
   const int v_lane = (4 * hi + (s16 >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+  // SWZ: the byte offsets of this lane's 8-byte pieces of 32-dim block db in
+  // rows 4 hi + s16 / 4 and 8 further (the same in every 16-row group)
+  int v_swz[SWZ ? 2 * DBLK : 1];
+  if constexpr (SWZ) {
+    const int r = 4 * hi + (s16 >> 2);
+    const int byte = 32 * ((lane >> 4) & 1) + 8 * (s16 & 3);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int c = (byte >> 4) + 4 * db;
+      v_swz[2 * db] = r * VROW + 16 * (c ^ lds_swizzle(r)) + (byte & 15);
+      v_swz[2 * db + 1] = (r + 8) * VROW + 16 * (c ^ lds_swizzle(r + 8)) + (byte & 15);
+    }
+  }
 
   // S^T = K Q^T for the two 32-key blocks of the K tile in stage pc
   auto scores = [&](auto pc, f32x16_t (&s)[2]) {
@@ -449,7 +482,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const frag kf = __builtin_bit_cast(
-            frag, *(FA_LDS u32x4_t*)(kb + k_lane + kb2 * 32 * KROW + st * 32));
+            frag, *(FA_LDS u32x4_t*)(kb + (SWZ ? k_swz[SWZ ? st : 0] : k_lane + st * 32) + kb2 * 32 * KROW));
         s[kb2] = M::mma(kf, qf[st], s[kb2]);
       }
   };
@@ -516,9 +549,11 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
       const frag pf = __builtin_bit_cast(frag, praw);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        FA_LDS char* p0 = vb + v_lane + (16 * u) * VROW + db * 64;
+        FA_LDS char* p0 = SWZ ? vb + v_swz[SWZ ? 2 * db : 0] + (16 * u) * VROW
+                              : vb + v_lane + (16 * u) * VROW + db * 64;
+        FA_LDS char* p1 = SWZ ? vb + v_swz[SWZ ? 2 * db + 1 : 0] + (16 * u) * VROW : p0 + 8 * VROW;
         const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p0);
-        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)(p0 + 8 * VROW));
+        const i16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p1);
         const u32x4_t vraw = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
                               __builtin_bit_cast(u32x2_t, up)[0], __builtin_bit_cast(u32x2_t, up)[1]};
         acc[db] = M::mma(__builtin_bit_cast(frag, vraw), pf, acc[db]);
