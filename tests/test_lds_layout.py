@@ -130,32 +130,37 @@ def test_forward_tile_strides(d):
         assert conflict_free(addrs, 8)
 
 
-def lds_swizzle(r):
-    """Slot permutation of the 16 chunks of a 256-byte row (the head_dim-128
-    forward with K/V loads two tiles ahead): chunk c of row r sits at slot
-    c ^ lds_swizzle(r)."""
-    return ((r & 3) << 2) | ((r >> 2) & 3)
+def lds_swizzle(r, rowb):
+    """Slot permutation of the chunks of an unpadded row of `rowb` bytes (the
+    head_dim-64/128 forward with K/V loads two tiles ahead): chunk c of row r
+    sits at slot c ^ lds_swizzle(r, rowb)."""
+    if rowb == 256:
+        return ((r & 3) << 2) | ((r >> 2) & 3)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
 
 
-def test_forward_swizzled_256_byte_rows():
-    """head_dim 128, 64-row K and V tiles at 256 bytes per row without padding:
-    (1) the 16 direct-to-LDS loads of 1 KiB place every chunk exactly once;
-    (2) the K row reads and the V transposing reads, addressed as the kernel
-    does, find the chunks of the unswizzled layout; (3) neither conflicts."""
-    R, rows, ksteps, dblk = 256, 64, 8, 4
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_swizzled_unpadded_rows(d):
+    """head_dim 64 / 128, 64-row K and V tiles at 2 d bytes per row without
+    padding: (1) the direct-to-LDS loads of 1 KiB place every chunk exactly
+    once; (2) the K row reads and the V transposing reads, addressed as the
+    kernel does, find the chunks of the unswizzled layout; (3) neither
+    conflicts."""
+    R, rows, ksteps, dblk = 2 * d, 64, d // 16, d // 32
+    nch = R // 16
     # (1) load slot -> (row, chunk): slot p of row r holds chunk p ^ lds_swizzle(r)
     placed = set()
-    for inst in range(16):
+    for inst in range(rows * nch // 64):
         for lane in range(64):
             slot = inst * 64 + lane
-            r, p = divmod(slot, 16)
-            placed.add((r, p ^ lds_swizzle(r)))
-    assert placed == {(r, c) for r in range(rows) for c in range(16)}
+            r, p = divmod(slot, nch)
+            placed.add((r, p ^ lds_swizzle(r, R)))
+    assert placed == {(r, c) for r in range(rows) for c in range(nch)}
 
     def chunk_at(addr):
         r, off = divmod(addr, R)
         p, b = divmod(off, 16)
-        return r, p ^ lds_swizzle(r), b
+        return r, p ^ lds_swizzle(r, R), b
 
     # (2) + (3) K row reads: lane (l32, hi), k-step st, 32-row block kb2
     for kb2 in range(2):
@@ -163,7 +168,7 @@ def test_forward_swizzled_256_byte_rows():
             addrs = []
             for lane in range(64):
                 l32, hi = lane & 31, lane >> 5
-                a = l32 * R + 16 * ((2 * st + hi) ^ lds_swizzle(l32)) + kb2 * 32 * R
+                a = l32 * R + 16 * ((2 * st + hi) ^ lds_swizzle(l32, R)) + kb2 * 32 * R
                 assert chunk_at(a) == (kb2 * 32 + l32, 2 * st + hi, 0)
                 addrs.append(a)
             for g in range(4):
@@ -178,7 +183,7 @@ def test_forward_swizzled_256_byte_rows():
                     r = 4 * hi + (s16 >> 2) + (8 if upper else 0)
                     byte = 32 * ((lane >> 4) & 1) + 8 * (s16 & 3)
                     c = (byte >> 4) + 4 * db
-                    a = r * R + 16 * (c ^ lds_swizzle(r)) + (byte & 15) + 16 * u * R
+                    a = r * R + 16 * (c ^ lds_swizzle(r, R)) + (byte & 15) + 16 * u * R
                     assert chunk_at(a) == (16 * u + r, c, byte & 15)
                     addrs.append(a)
                 for g in range(2):

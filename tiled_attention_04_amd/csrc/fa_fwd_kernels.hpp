@@ -173,12 +173,18 @@ constexpr int tr_row_stride(int min_bytes) {
   return st;
 }
 
-// Slot permutation of the 16 chunks of a 256-byte row r: the high two bits
-// of the chunk index are XORed with r % 4, the low two with (r / 4) % 4.
-// 16 consecutive rows read at one chunk land on 16 distinct slots (row
-// reads of 16 lanes per cycle), and the four rows of a transposing read's
-// 32 lanes land in four distinct 64-byte windows.
-__device__ __host__ constexpr int lds_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Slot permutation of the 16-byte chunks of an unpadded row r of ROWB bytes.
+// 256-byte rows: the high two bits of the chunk index are XORed with r % 4,
+// the low two with (r / 4) % 4.  128-byte rows (two per 256-byte bank
+// window): bit 2 with (r / 2) % 2, the low two with (r / 4) % 4.  Either
+// way 16 consecutive rows read at one chunk land on 16 distinct bank groups
+// (row reads of 16 lanes per cycle), and the four rows of a transposing
+// read's 32 lanes cover all 64 banks.
+template <int ROWB>
+__device__ __host__ constexpr int lds_swizzle(int r) {
+  static_assert(ROWB == 256 || ROWB == 128, "swizzled row widths");
+  return ROWB == 256 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // ---------------------------------------------------------------------------
 // Buffer-resource helpers.  A raw buffer load whose byte offset lies at or
@@ -240,12 +246,12 @@ struct Tile16 {
   // chunk of 32 consecutive rows fall on distinct bank groups.
   // V rows: stride = 64 or 192 (mod 256) bytes, so the rows gathered by a
   // transposing read fall on distinct banks.
-  // SWZ (head_dim 128): unpadded 256-byte rows, 16-byte chunk c of row r at
-  // slot c ^ lds_swizzle(r) instead: 16 loads of 1 KiB per tile, which
-  // eight waves issue two each.
+  // SWZ (head_dim 64 and 128): unpadded rows of 128 or 256 bytes, 16-byte
+  // chunk c of row r at slot c ^ lds_swizzle(r) instead: 8 or 16 loads of
+  // 1 KiB per tile, which eight waves issue one or two each.
   static constexpr int KROW = SWZ ? D * 2 : D * 2 + 16;
   static constexpr int VROW = SWZ ? DBLK * 64 : tr_row_stride(DBLK * 64);
-  static_assert(!SWZ || (KROW == 256 && VROW == 256), "the swizzle is for 256-byte rows");
+  static_assert(!SWZ || (KROW == VROW && (KROW == 256 || KROW == 128)), "swizzled row widths");
   static constexpr int KSLOTS = KROW / 16;     // 16-byte LDS slots per K row (incl. padding)
   static constexpr int VSLOTS = VROW / 16;
   static constexpr int KINSTR = BN * KSLOTS / 64;  // wave-wide 1 KiB loads per K tile
@@ -284,7 +290,7 @@ __device__ __forceinline__ FA_LDS char* lds_object() {
 // steps to land.
 template <typename T, int D, int NW, bool XB = false, bool DEEP = false>
 __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
-  constexpr bool SWZ = DEEP && D == 128;  // unpadded swizzled rows (no surplus loads)
+  constexpr bool SWZ = DEEP;  // (head_dim 64 and 128) unpadded swizzled rows: no surplus loads
   using G = Tile16<T, D, NW, XB, SWZ>;
   using M = Mfma<T>;
   typedef typename M::frag frag;
@@ -375,14 +381,16 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   for (int n = 0; n < G::KPER; ++n) {
     const int slot = kinstr(n) * 64 + lane;
     const int row = slot / G::KSLOTS;
-    const int ch = (slot - row * G::KSLOTS) ^ (SWZ ? lds_swizzle(row) : 0);  // the chunk this slot holds
+    int ch = slot - row * G::KSLOTS;
+    if constexpr (SWZ) ch ^= lds_swizzle<KROW>(row);  // the chunk this slot holds
     koff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.k_ss * 2 + ch * 16) : kOutOfRange;
   }
 #pragma unroll
   for (int n = 0; n < G::VPER; ++n) {
     const int slot = vinstr(n) * 64 + lane;
     const int row = slot / G::VSLOTS;
-    const int ch = (slot - row * G::VSLOTS) ^ (SWZ ? lds_swizzle(row) : 0);
+    int ch = slot - row * G::VSLOTS;
+    if constexpr (SWZ) ch ^= lds_swizzle<VROW>(row);
     voff[n] = ch * 8 < a.head_dim ? (uint32_t)(row * (int32_t)a.v_ss * 2 + ch * 16) : kOutOfRange;
     vlive[n] = ch * 8 < D;
   }
@@ -454,7 +462,7 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
   int k_swz[SWZ ? KSTEPS : 1];
   if constexpr (SWZ) {
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) k_swz[st] = l32 * KROW + 16 * ((2 * st + hi) ^ lds_swizzle(l32));
+    for (int st = 0; st < KSTEPS; ++st) k_swz[st] = l32 * KROW + 16 * ((2 * st + hi) ^ lds_swizzle<KROW>(l32));
   }
   const int s16 = lane & 15;
   const int v_lane = (4 * hi + (s16 >> 2)) * VROW + (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
@@ -467,8 +475,8 @@ __device__ __forceinline__ void fa_fwd_16bit_body(const FwdArgs& a) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
       const int c = (byte >> 4) + 4 * db;
-      v_swz[2 * db] = r * VROW + 16 * (c ^ lds_swizzle(r)) + (byte & 15);
-      v_swz[2 * db + 1] = (r + 8) * VROW + 16 * (c ^ lds_swizzle(r + 8)) + (byte & 15);
+      v_swz[2 * db] = r * VROW + 16 * (c ^ lds_swizzle<VROW>(r)) + (byte & 15);
+      v_swz[2 * db + 1] = (r + 8) * VROW + 16 * (c ^ lds_swizzle<VROW>(r + 8)) + (byte & 15);
     }
   }
 
